@@ -1,0 +1,202 @@
+"""Python view of the CPU oracle (oracle/mx_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+benchmark's CPU-baseline leg, never by the product library.  It loads
+``oracle/libmx_oracle.so`` (built with gcc by :func:`build`) and marshals numpy
+arrays to it; every piece of arithmetic lives in the C file.
+
+Arrays: e4m3/e2m1/code bytes are ``uint8``; bf16 values travel as their
+``uint16`` bit patterns; results of the linear layers are ``float64``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "mx_oracle.c")
+LIB = os.path.join(HERE, "libmx_oracle.so")
+
+E4M3, E2M1 = 0, 1
+ROW32, BLK32 = 0, 1
+RULE_OCP, RULE_CEIL448 = 0, 1
+ACT_BF16, ACT_MXFP8 = 0, 1
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, OpenMP over rows)."""
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-Wall",
+           "-o", LIB + ".tmp", SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+def lib() -> C.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        _lib = C.CDLL(LIB)
+        _declare(_lib)
+    return _lib
+
+
+def _declare(L):
+    i64, i32, dbl = C.c_int64, C.c_int, C.c_double
+    p = C.c_void_p
+    L.orc_e4m3_value.argtypes = [i32]; L.orc_e4m3_value.restype = dbl
+    L.orc_e2m1_value.argtypes = [i32]; L.orc_e2m1_value.restype = dbl
+    L.orc_e8m0_value.argtypes = [i32]; L.orc_e8m0_value.restype = dbl
+    L.orc_bf16_value.argtypes = [C.c_uint16]; L.orc_bf16_value.restype = dbl
+    L.orc_e4m3_round.argtypes = [dbl]; L.orc_e4m3_round.restype = i32
+    L.orc_act_code.argtypes = [dbl, i32]; L.orc_act_code.restype = i32
+    L.orc_quant_act.argtypes = [i64, i64, p, i64, p, i64, p, i64, i32]
+    L.orc_quant_act.restype = None
+    L.orc_padded_k.argtypes = [i64]; L.orc_padded_k.restype = i64
+    L.orc_packed_sizes.argtypes = [i32, i32, i64, i64, i64, p, p]
+    L.orc_packed_sizes.restype = i32
+    L.orc_pack_weights.argtypes = [i32, i32, i64, i64, i64, p, p, p, p]
+    L.orc_pack_weights.restype = i32
+    L.orc_weight.argtypes = [i32, i32, i64, i64, i64, p, p, i64, i64, i64]
+    L.orc_weight.restype = dbl
+    L.orc_linear.argtypes = [i32, i32, i64, i64, p, p, i64, i32, p, i64, p, i64,
+                             p, i64, p, p]
+    L.orc_linear.restype = None
+    L.orc_linear_pairs.argtypes = [i32, i32, i64, i64, p, p, i32, p, i64, p, i64,
+                                   p, i64, p, i64, p, p, p]
+    L.orc_linear_pairs.restype = None
+    L.orc_moe_linear.argtypes = [i32, i64, i64, i64, p, p, i64, i64, p, i64, p,
+                                 p, p]
+    L.orc_moe_linear.restype = None
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# --- scalar decoders ----------------------------------------------------
+
+def e4m3_value(b: int) -> float:
+    return lib().orc_e4m3_value(int(b))
+
+
+def e2m1_value(n: int) -> float:
+    return lib().orc_e2m1_value(int(n))
+
+
+def e8m0_value(c: int) -> float:
+    return lib().orc_e8m0_value(int(c))
+
+
+def bf16_value(bits: int) -> float:
+    return lib().orc_bf16_value(int(bits))
+
+
+def e4m3_round(v: float) -> int:
+    return lib().orc_e4m3_round(float(v))
+
+
+def act_code(amax: float, rule: int) -> int:
+    return lib().orc_act_code(float(amax), int(rule))
+
+
+# --- array entry points ---------------------------------------------------
+
+def quant_act(x_bits: np.ndarray, rule: int):
+    """x_bits uint16 [M, K] (bf16 patterns) -> (xq uint8 [M, K], codes uint8 [M, K/32])."""
+    x = _c(x_bits, np.uint16)
+    M, K = x.shape
+    xq = np.zeros((M, K), np.uint8)
+    codes = np.zeros((M, K // 32), np.uint8)
+    lib().orc_quant_act(M, K, _ptr(x), K, _ptr(xq), K, _ptr(codes), K // 32, rule)
+    return xq, codes
+
+
+def padded_k(K: int) -> int:
+    return lib().orc_padded_k(K)
+
+
+def packed_sizes(elem, layout, E, N, K):
+    wb, cb = C.c_int64(), C.c_int64()
+    rc = lib().orc_packed_sizes(elem, layout, E, N, K, C.byref(wb), C.byref(cb))
+    if rc:
+        raise ValueError(f"shape not packable: elem={elem} layout={layout} E={E} N={N} K={K}")
+    return wb.value, cb.value
+
+
+def pack_weights(elem, layout, E, N, K, w, codes):
+    """Standard bytes + codes -> (packed weight bytes, packed codes), 1-D uint8."""
+    wb, cb = packed_sizes(elem, layout, E, N, K)
+    w = _c(w, np.uint8)
+    codes = _c(codes, np.uint8)
+    wp = np.empty(wb, np.uint8)
+    cp = np.empty(cb, np.uint8)
+    rc = lib().orc_pack_weights(elem, layout, E, N, K, _ptr(w), _ptr(codes), _ptr(wp), _ptr(cp))
+    if rc:
+        raise ValueError("pack failed")
+    return wp, cp
+
+
+def weight(elem, layout, E, N, K, w, codes, e, n, k) -> float:
+    w = _c(w, np.uint8)
+    codes = _c(codes, np.uint8)
+    return lib().orc_weight(elem, layout, E, N, K, _ptr(w), _ptr(codes), e, n, k)
+
+
+def linear(elem, layout, N, K, w, codes, M, act, x=None, xq=None, xcodes=None, bias=None):
+    """fp64 y [M, N] = a . Wf^T (+ bias); x bf16 bits [M, K] or (xq, xcodes)."""
+    w = _c(w, np.uint8)
+    codes = _c(codes, np.uint8)
+    x = _c(x, np.uint16)
+    xq = _c(xq, np.uint8)
+    xcodes = _c(xcodes, np.uint8)
+    bias = _c(bias, np.uint16)
+    y = np.empty((M, N), np.float64)
+    lib().orc_linear(elem, layout, N, K, _ptr(w), _ptr(codes), M, act,
+                     _ptr(x), K, _ptr(xq), K, _ptr(xcodes), K // 32, _ptr(bias), _ptr(y))
+    return y
+
+
+def linear_pairs(elem, layout, N, K, w, codes, act, ms, ns, x=None, xq=None,
+                 xcodes=None, bias=None):
+    """fp64 y[ms[p], ns[p]] for each pair p."""
+    w = _c(w, np.uint8)
+    codes = _c(codes, np.uint8)
+    x = _c(x, np.uint16)
+    xq = _c(xq, np.uint8)
+    xcodes = _c(xcodes, np.uint8)
+    bias = _c(bias, np.uint16)
+    ms = _c(ms, np.int64)
+    ns = _c(ns, np.int64)
+    out = np.empty(len(ms), np.float64)
+    lib().orc_linear_pairs(elem, layout, N, K, _ptr(w), _ptr(codes), act,
+                           _ptr(x), K, _ptr(xq), K, _ptr(xcodes), K // 32,
+                           _ptr(bias), len(ms), _ptr(ms), _ptr(ns), _ptr(out))
+    return out
+
+
+def moe_linear(elem, E, N, K, w, codes, x, ids, weights=None):
+    """fp64 per-slot y [T, topk, N], or combined [T, N] when weights is given."""
+    w = _c(w, np.uint8)
+    codes = _c(codes, np.uint8)
+    x = _c(x, np.uint16)
+    ids = _c(ids, np.int32)
+    T, topk = ids.shape
+    weights = _c(weights, np.float32)
+    shape = (T, N) if weights is not None else (T, topk, N)
+    y = np.empty(shape, np.float64)
+    lib().orc_moe_linear(elem, E, N, K, _ptr(w), _ptr(codes), T, topk, _ptr(x),
+                         x.shape[1], _ptr(ids), _ptr(weights), _ptr(y))
+    return y

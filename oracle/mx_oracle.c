@@ -1,0 +1,444 @@
+/*
+ * mx_oracle.c -- plain, slow CPU reference ("oracle") for the block-scaled
+ * (OCP microscaling) linear layer y = x . W^T.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the tests, the smoke check and the benchmark's CPU
+ * baseline leg do.  It shares no code, header, table or constant with the
+ * HIP library; both sides are written independently from the definitions
+ * below.
+ *
+ * Sources (web pages; cited by page title and section):
+ *   [weights942]   vllm.models.deepseek_v41.amd.mono.weights942
+ *   [rocm_native]  vllm.model_executor.kernels.linear.mxfp8.rocm_native
+ *   [a16w4]        vllm.models.minimax_m3.amd.specialized_decode.mono.a16w4
+ *   [fused_layout] vllm.models.deepseek_v41.common.ops.fused_layout
+ *
+ * Arithmetic: every real value is carried in IEEE binary64.  Decoding is
+ * exact, products of decoded operands are exact in binary64, and sums are
+ * taken in index order.  Nothing is fused, blocked or reordered.
+ *
+ * Readings taken where the pages leave a step open (each one is listed with
+ * its justification in the design notes of the repository):
+ *   R1  activation scale rule "ocp": shared exponent floor(log2 amax) - 8
+ *       (8 = exponent of the largest e4m3 normal, 448 = 1.75 * 2^8); element
+ *       conversion round-to-nearest-even with saturation to +-448.
+ *   R2  activation scale rule "ceil448": the rule [rocm_native] _quant_mxfp8_tile
+ *       states, ceil(log2(max(amax, TINY) / 448)) + 127 clamped to [0, 254],
+ *       with TINY = 2^-126 and FP8_MAX = 448 (both undefined on the page).
+ *   R3  a zero result keeps the sign of its input (-0 -> 0x80).
+ *   R4  K is padded to a multiple of 128 with zero bytes and scale code 128
+ *       ([weights942] dense_copy); padding never enters a sum.
+ *   R5  MoE ids outside [0, E) give all-zero output rows.
+ *
+ * Parity pins: every function here is checked in tests/test_oracle_*.py
+ * against closed forms, brute force and exact rational arithmetic.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_E4M3 = 0, ORC_E2M1 = 1 };
+enum { ORC_ROW32 = 0, ORC_BLK32 = 1 };
+enum { ORC_RULE_OCP = 0, ORC_RULE_CEIL448 = 1 };
+enum { ORC_ACT_BF16 = 0, ORC_ACT_MXFP8 = 1 };
+
+/* ------------------------------------------------------------------ */
+/* Element and scale decoding                                          */
+/* ------------------------------------------------------------------ */
+
+/* OCP E4M3 byte: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits.
+ * Exponent field 0 is subnormal: 2^-6 * m/8.  0x7F and 0xFF are NaN; the
+ * largest finite magnitude is 0x7E = 1.75 * 2^8 = 448.  ([weights942] module
+ * notes on OCP bytes; [rocm_native] float8e4nv.) */
+double orc_e4m3_value(int byte)
+{
+    int s = (byte >> 7) & 1, e = (byte >> 3) & 15, m = byte & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m / 8.0, -6);
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -mag : mag;
+}
+
+/* OCP E2M1 nibble: 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit.
+ * Exponent field 0 is subnormal: m/2.  Magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6.
+ * ([a16w4] dequant: packed two per byte, low nibble first.) */
+double orc_e2m1_value(int nibble)
+{
+    int s = (nibble >> 3) & 1, e = (nibble >> 1) & 3, m = nibble & 1;
+    double mag;
+    if (e == 0)
+        mag = (double)m / 2.0;
+    else
+        mag = ldexp(1.0 + (double)m / 2.0, e - 1);
+    return s ? -mag : mag;
+}
+
+/* E8M0 scale code: the power of two 2^(code - 127); code 255 is NaN.
+ * ([weights942] ocp_from_dequant: value = e4m3 value x 2^(code - 127).) */
+double orc_e8m0_value(int code)
+{
+    if (code == 255)
+        return NAN;
+    return ldexp(1.0, code - 127);
+}
+
+/* A bfloat16 bit pattern is the upper half of a binary32 pattern. */
+double orc_bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* ------------------------------------------------------------------ */
+/* E4M3 rounding                                                       */
+/* ------------------------------------------------------------------ */
+
+/* Nearest finite E4M3 value to v, ties to the code whose mantissa LSB is 0,
+ * saturating at +-448 (R1), zero keeping the sign of v (R3).  The 127
+ * non-negative finite codes 0x00..0x7E are increasing in value, so the
+ * nearest code is found by locating v between two neighbours. */
+int orc_e4m3_round(double v)
+{
+    int sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs(v);
+    int lo, hi, mid, pick;
+    double dlo, dhi;
+    if (a >= 448.0)
+        return sign | 0x7E;
+    /* largest code lo with value(lo) <= a */
+    lo = 0;
+    hi = 0x7E;
+    while (lo < hi) {
+        mid = (lo + hi + 1) / 2;
+        if (orc_e4m3_value(mid) <= a)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    if (orc_e4m3_value(lo) == a)
+        return sign | lo;
+    dlo = a - orc_e4m3_value(lo);
+    dhi = orc_e4m3_value(lo + 1) - a;
+    if (dlo < dhi)
+        pick = lo;
+    else if (dhi < dlo)
+        pick = lo + 1;
+    else
+        pick = (lo & 1) ? lo + 1 : lo;
+    return sign | pick;
+}
+
+/* ------------------------------------------------------------------ */
+/* Activation quantization (per token, per 32-element K block)          */
+/* ------------------------------------------------------------------ */
+
+/* E8M0 code of a block whose largest magnitude is amax.
+ *   ocp     (R1): code = floor(log2 amax) - 8 + 127, clamped to [0, 254];
+ *                 amax == 0 gives code 0.
+ *   ceil448 (R2): [rocm_native] _quant_mxfp8_tile -- the smallest n with
+ *                 448 * 2^n >= max(amax, TINY); code = n + 127 clamped to
+ *                 [0, 254].
+ * Both exponents start from a log2 guess and are then settled by exact
+ * comparisons against powers of two, so the guess's rounding cannot matter. */
+int orc_act_code(double amax, int rule)
+{
+    int n;
+    if (rule == ORC_RULE_OCP) {
+        if (amax == 0.0)
+            return 0;
+        n = (int)floor(log2(amax));
+        while (ldexp(1.0, n) > amax) /* largest n with 2^n <= amax */
+            n--;
+        while (ldexp(1.0, n + 1) <= amax)
+            n++;
+        n = n - 8 + 127;
+    } else {
+        double a = amax > ldexp(1.0, -126) ? amax : ldexp(1.0, -126);
+        n = (int)ceil(log2(a / 448.0));
+        while (ldexp(448.0, n - 1) >= a) /* smallest n with 448 * 2^n >= a */
+            n--;
+        while (ldexp(448.0, n) < a)
+            n++;
+        n = n + 127;
+    }
+    if (n < 0)
+        n = 0;
+    if (n > 254)
+        n = 254;
+    return n;
+}
+
+/* Quantize x (bf16 bits, [M, K] with row stride ldx) to e4m3 bytes xq
+ * ([M, K], stride ldq) and row-major E8M0 codes ([M, K/32], stride ldc):
+ * for each row m and block b, code = orc_act_code(max |x|), and each
+ * element is RNE_e4m3(x * 2^(127 - code)), the product exact in binary64.
+ * ([rocm_native] module notes: per-token quantization with row-major
+ * [M, K/32] codes; _quant_mxfp8_tile for the per-block steps.) */
+void orc_quant_act(int64_t M, int64_t K, const uint16_t *x, int64_t ldx,
+                   uint8_t *xq, int64_t ldq, uint8_t *codes, int64_t ldc,
+                   int rule)
+{
+    int64_t m, b, i;
+    for (m = 0; m < M; m++) {
+        for (b = 0; b < K / 32; b++) {
+            double amax = 0.0;
+            int code;
+            double mul;
+            for (i = 0; i < 32; i++) {
+                double a = fabs(orc_bf16_value(x[m * ldx + 32 * b + i]));
+                if (a > amax)
+                    amax = a;
+            }
+            code = orc_act_code(amax, rule);
+            mul = ldexp(1.0, 127 - code);
+            codes[m * ldc + b] = (uint8_t)code;
+            for (i = 0; i < 32; i++) {
+                double v = orc_bf16_value(x[m * ldx + 32 * b + i]) * mul;
+                xq[m * ldq + 32 * b + i] = (uint8_t)orc_e4m3_round(v);
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Packed weight and code layouts                                      */
+/* ------------------------------------------------------------------ */
+/*
+ * Notation: E experts (1 for a dense layer), N rows per expert, K values per
+ * row, Kp = K rounded up to 128 (R4), S = Kp / 128 "steps", T = N / 16
+ * "tiles" of 16 rows, Q = ceil(S / 4) "quads" of four steps.  A lane index
+ * l in [0, 64) of a 64-wide wavefront is split as l = 16 j + r.
+ *
+ * Weights W-T16.  For each (expert e, tile t, step s) a chunk of 16 rows x
+ * 128 K values: 2048 bytes for E4M3, 1024 for E2M1.  Lane l owns row
+ * 16 t + r and the 32-value block 4 s + j of that row; its bytes sit at
+ * 16 l + 1024 h (h = 0, 1 for E4M3; h = 0 for E2M1), so every 16-byte load
+ * of the wavefront reads 1 KB contiguous.  This is the tile-major idea of
+ * [weights942] dense_copy and fp4_tile_major, with the one-block-per-lane
+ * ownership of [a16w4] (module notes).  Padding bytes are 0.
+ *
+ *   E4M3: wp[((e T + t) S + s) 2048 + 1024 h + 16 l + c]
+ *           = w[e][16 t + r][128 s + 32 j + 16 h + c]
+ *   E2M1: wp[((e T + t) S + s) 1024 + 16 l + c]
+ *           = w[e][16 t + r][byte 64 s + 16 j + c]       (low nibble = even K)
+ *
+ * Codes ROW32 ([E N, K/32] in) -> C-T16.  For each (expert, tile, quad) 256
+ * bytes; lane l's dword holds the codes of its row for the blocks it owns in
+ * the quad's four steps, step 4 q + u in byte u.  A lane group of 16 lanes
+ * reads 64 contiguous bytes (the staging idea of [weights942]
+ * codes_tile_rounds and the per-lane dwords of [a16w4] scale_loads).
+ *
+ *   cp[((e T + t) Q + q) 256 + 4 l + u] = codes[e N + 16 t + r][4 (4 q + u) + j]
+ *
+ * Codes BLK32 ([E N/32, K/32] in) -> row-major [E N/32, Kp/32].
+ * Every code of a block outside [0, K/32) is 128 (R4).
+ */
+
+int64_t orc_padded_k(int64_t K) { return (K + 127) / 128 * 128; }
+
+/* 0 on success, 1 for a shape the layout does not cover. */
+int orc_packed_sizes(int elem, int layout, int64_t E, int64_t N, int64_t K,
+                     int64_t *w_bytes, int64_t *c_bytes)
+{
+    int64_t Kp = orc_padded_k(K), S = Kp / 128, Q = (S + 3) / 4;
+    if (E < 1 || N < 1 || K < 32 || K % 32 != 0 || N % 16 != 0)
+        return 1;
+    if (layout == ORC_BLK32 && N % 32 != 0)
+        return 1;
+    *w_bytes = E * N * (elem == ORC_E4M3 ? Kp : Kp / 2);
+    if (layout == ORC_ROW32)
+        *c_bytes = E * (N / 16) * Q * 256;
+    else
+        *c_bytes = E * (N / 32) * (Kp / 32);
+    return 0;
+}
+
+int orc_pack_weights(int elem, int layout, int64_t E, int64_t N, int64_t K,
+                     const uint8_t *w, const uint8_t *codes, uint8_t *wp,
+                     uint8_t *cp)
+{
+    int64_t Kp = orc_padded_k(K), S = Kp / 128, Q = (S + 3) / 4, T = N / 16;
+    int64_t wb, cb, e, t, s, q, l, h, c, u;
+    if (orc_packed_sizes(elem, layout, E, N, K, &wb, &cb))
+        return 1;
+    for (e = 0; e < E; e++)
+        for (t = 0; t < T; t++)
+            for (s = 0; s < S; s++)
+                for (l = 0; l < 64; l++) {
+                    int64_t r = l % 16, j = l / 16, row = 16 * t + r;
+                    if (elem == ORC_E4M3) {
+                        for (h = 0; h < 2; h++)
+                            for (c = 0; c < 16; c++) {
+                                int64_t k = 128 * s + 32 * j + 16 * h + c;
+                                int64_t dst = ((e * T + t) * S + s) * 2048 + 1024 * h + 16 * l + c;
+                                wp[dst] = k < K ? w[(e * N + row) * K + k] : 0;
+                            }
+                    } else {
+                        for (c = 0; c < 16; c++) {
+                            int64_t byte = 64 * s + 16 * j + c;
+                            int64_t dst = ((e * T + t) * S + s) * 1024 + 16 * l + c;
+                            wp[dst] = byte < K / 2 ? w[(e * N + row) * (K / 2) + byte] : 0;
+                        }
+                    }
+                }
+    if (layout == ORC_ROW32) {
+        for (e = 0; e < E; e++)
+            for (t = 0; t < T; t++)
+                for (q = 0; q < Q; q++)
+                    for (l = 0; l < 64; l++)
+                        for (u = 0; u < 4; u++) {
+                            int64_t r = l % 16, j = l / 16;
+                            int64_t blk = 4 * (4 * q + u) + j;
+                            int64_t dst = ((e * T + t) * Q + q) * 256 + 4 * l + u;
+                            cp[dst] = blk < K / 32 ? codes[(e * N + 16 * t + r) * (K / 32) + blk] : 128;
+                        }
+    } else {
+        int64_t R, b;
+        for (R = 0; R < E * N / 32; R++)
+            for (b = 0; b < Kp / 32; b++)
+                cp[R * (Kp / 32) + b] = b < K / 32 ? codes[R * (K / 32) + b] : 128;
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Dequantized operands                                                */
+/* ------------------------------------------------------------------ */
+
+/* Weight value Wf[e][n][k] = dec(w) * 2^(code - 127) from the standard
+ * (unpacked) layouts: E4M3 bytes [E, N, K] or E2M1 bytes [E, N, K/2] (value
+ * k in byte k/2, low nibble for even k); codes [E N, K/32] (ROW32) or
+ * [E N/32, K/32] (BLK32).  ([weights942] ocp_from_dequant; [a16w4] dequant.) */
+double orc_weight(int elem, int layout, int64_t E, int64_t N, int64_t K,
+                  const uint8_t *w, const uint8_t *codes, int64_t e, int64_t n,
+                  int64_t k)
+{
+    double v;
+    int code;
+    (void)E;
+    if (elem == ORC_E4M3) {
+        v = orc_e4m3_value(w[(e * N + n) * K + k]);
+    } else {
+        int byte = w[(e * N + n) * (K / 2) + k / 2];
+        v = orc_e2m1_value(k % 2 == 0 ? (byte & 15) : (byte >> 4));
+    }
+    if (layout == ORC_ROW32)
+        code = codes[(e * N + n) * (K / 32) + k / 32];
+    else
+        code = codes[((e * N + n) / 32) * (K / 32) + k / 32];
+    return v * orc_e8m0_value(code);
+}
+
+/* Activation value a[m][k]: the bf16 value itself (A16), or the MXFP8 pair
+ * dec(xq) * 2^(xcode - 127) with row-major codes (W8A8). */
+double orc_activation(int act, const uint16_t *x, int64_t ldx, const uint8_t *xq,
+                      int64_t ldq, const uint8_t *xc, int64_t ldc, int64_t m,
+                      int64_t k)
+{
+    if (act == ORC_ACT_BF16)
+        return orc_bf16_value(x[m * ldx + k]);
+    return orc_e4m3_value(xq[m * ldq + k]) * orc_e8m0_value(xc[m * ldc + k / 32]);
+}
+
+/* ------------------------------------------------------------------ */
+/* Linear layer                                                        */
+/* ------------------------------------------------------------------ */
+
+/* y[m][n] = sum_{k < K} a[m][k] Wf[n][k] (+ bias[n]), binary64, k ascending.
+ * ([rocm_native] RocmDotScaledMxfp8LinearKernel.apply_weights: out = x W^T,
+ * then + bias.)  Rows of Wf are decoded once per n; the sums are unchanged. */
+void orc_linear(int elem, int layout, int64_t N, int64_t K, const uint8_t *w,
+                const uint8_t *codes, int64_t M, int act, const uint16_t *x,
+                int64_t ldx, const uint8_t *xq, int64_t ldq, const uint8_t *xc,
+                int64_t ldc, const uint16_t *bias, double *y)
+{
+    double *a = (double *)malloc(sizeof(double) * (size_t)(M * K));
+    int64_t m, k, n;
+    for (m = 0; m < M; m++)
+        for (k = 0; k < K; k++)
+            a[m * K + k] = orc_activation(act, x, ldx, xq, ldq, xc, ldc, m, k);
+#pragma omp parallel for schedule(static)
+    for (n = 0; n < N; n++) {
+        double *wrow = (double *)malloc(sizeof(double) * (size_t)K);
+        int64_t mm, kk;
+        for (kk = 0; kk < K; kk++)
+            wrow[kk] = orc_weight(elem, layout, 1, N, K, w, codes, 0, n, kk);
+        for (mm = 0; mm < M; mm++) {
+            double s = 0.0;
+            for (kk = 0; kk < K; kk++)
+                s += a[mm * K + kk] * wrow[kk];
+            if (bias)
+                s += orc_bf16_value(bias[n]);
+            y[mm * N + n] = s;
+        }
+        free(wrow);
+    }
+    free(a);
+}
+
+/* The same sums, for a list of (m, n) pairs only (large shapes). */
+void orc_linear_pairs(int elem, int layout, int64_t N, int64_t K,
+                      const uint8_t *w, const uint8_t *codes, int act,
+                      const uint16_t *x, int64_t ldx, const uint8_t *xq,
+                      int64_t ldq, const uint8_t *xc, int64_t ldc,
+                      const uint16_t *bias, int64_t npairs, const int64_t *ms,
+                      const int64_t *ns, double *out)
+{
+    int64_t p;
+#pragma omp parallel for schedule(static)
+    for (p = 0; p < npairs; p++) {
+        double s = 0.0;
+        int64_t kk;
+        for (kk = 0; kk < K; kk++)
+            s += orc_activation(act, x, ldx, xq, ldq, xc, ldc, ms[p], kk) *
+                 orc_weight(elem, layout, 1, N, K, w, codes, 0, ns[p], kk);
+        if (bias)
+            s += orc_bf16_value(bias[ns[p]]);
+        out[p] = s;
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Grouped MoE linear                                                  */
+/* ------------------------------------------------------------------ */
+
+/* For every token t and slot k of its top-k routing, the row
+ *   y[t][k][:] = x[t] . Wf[id[t][k]]^T                       (per slot), or
+ *   out[t][:]  = sum_k weight[t][k] y[t][k][:], k ascending  (combined),
+ * in binary64.  Expert weights are [E, N, K] in the standard layouts with
+ * ROW32 codes [E N, K/32] ([weights942] moe_copies, expert tensors before
+ * conversion).  An id outside [0, E) contributes a zero row (R5). */
+void orc_moe_linear(int elem, int64_t E, int64_t N, int64_t K, const uint8_t *w,
+                    const uint8_t *codes, int64_t T, int64_t topk,
+                    const uint16_t *x, int64_t ldx, const int32_t *ids,
+                    const float *weights, double *y)
+{
+    int64_t n;
+    int64_t rows = weights ? T : T * topk;
+    memset(y, 0, sizeof(double) * (size_t)(rows * N));
+#pragma omp parallel for schedule(static)
+    for (n = 0; n < N; n++) {
+        int64_t t, k, kk;
+        for (t = 0; t < T; t++)
+            for (k = 0; k < topk; k++) {
+                int32_t e = ids[t * topk + k];
+                double s = 0.0;
+                if (e >= 0 && e < E)
+                    for (kk = 0; kk < K; kk++)
+                        s += orc_bf16_value(x[t * ldx + kk]) *
+                             orc_weight(elem, ORC_ROW32, E, N, K, w, codes, e, n, kk);
+                if (weights)
+                    y[t * N + n] += (double)weights[t * topk + k] * s;
+                else
+                    y[(t * topk + k) * N + n] = s;
+            }
+    }
+}
