@@ -218,15 +218,19 @@ void orc_quant_act(int64_t M, int64_t K, const uint16_t *x, int64_t ldx,
  * l in [0, 64) of a 64-wide wavefront is split as l = 16 j + r.
  *
  * Weights W-T16.  For each (expert e, tile t, step s) a chunk of 16 rows x
- * 128 K values: 2048 bytes for E4M3, 1024 for E2M1.  Lane l owns row
- * 16 t + r and the 32-value block 4 s + j of that row; its bytes sit at
- * 16 l + 1024 h (h = 0, 1 for E4M3; h = 0 for E2M1), so every 16-byte load
- * of the wavefront reads 1 KB contiguous.  This is the tile-major idea of
- * [weights942] dense_copy and fp4_tile_major, with the one-block-per-lane
- * ownership of [a16w4] (module notes).  Padding bytes are 0.
+ * 128 K values: 2048 bytes for E4M3, 1024 for E2M1.  Lane l reads 16-byte
+ * pieces at 16 l (+ 1024 for the second E4M3 half), so every 16-byte load of
+ * the wavefront reads 1 KB contiguous: the tile-major idea of [weights942]
+ * dense_copy and fp4_tile_major.  Padding bytes are 0.
+ *   E4M3: lane l holds row 16 t + r, K 16 j .. 16 j + 15 of the step in its
+ *         first half and K 64 + 16 j .. + 15 in its second half -- the K
+ *         order in which a gfx950 16x16x128 scaled matrix-core operand lane
+ *         holds its 32 bytes (lane group j's scale covers K block j).
+ *   E2M1: lane l holds row 16 t + r, the whole 32-value block 4 s + j (one
+ *         code group a lane), as in [a16w4] (module notes).
  *
  *   E4M3: wp[((e T + t) S + s) 2048 + 1024 h + 16 l + c]
- *           = w[e][16 t + r][128 s + 32 j + 16 h + c]
+ *           = w[e][16 t + r][128 s + 64 h + 16 j + c]
  *   E2M1: wp[((e T + t) S + s) 1024 + 16 l + c]
  *           = w[e][16 t + r][byte 64 s + 16 j + c]       (low nibble = even K)
  *
@@ -277,7 +281,7 @@ int orc_pack_weights(int elem, int layout, int64_t E, int64_t N, int64_t K,
                     if (elem == ORC_E4M3) {
                         for (h = 0; h < 2; h++)
                             for (c = 0; c < 16; c++) {
-                                int64_t k = 128 * s + 32 * j + 16 * h + c;
+                                int64_t k = 128 * s + 64 * h + 16 * j + c;
                                 int64_t dst = ((e * T + t) * S + s) * 2048 + 1024 * h + 16 * l + c;
                                 wp[dst] = k < K ? w[(e * N + row) * K + k] : 0;
                             }

@@ -28,8 +28,8 @@ def _ref_weights(elem, E, N, K, w):
     Kp = -(-K // 128) * 128
     S, T = Kp // 128, N // 16
     if elem == E4M3:
-        v = _pad_cols(w.reshape(E, N, K), Kp, 0).reshape(E, T, 16, S, 4, 2, 16)
-        return v.transpose(0, 1, 3, 5, 4, 2, 6).reshape(-1)   # [e,t,s,h,j,r,c]
+        v = _pad_cols(w.reshape(E, N, K), Kp, 0).reshape(E, T, 16, S, 2, 4, 16)
+        return v.transpose(0, 1, 3, 4, 5, 2, 6).reshape(-1)   # [e,t,s,h,j,r,c]
     v = _pad_cols(w.reshape(E, N, K // 2), Kp // 2, 0).reshape(E, T, 16, S, 4, 16)
     return v.transpose(0, 1, 3, 4, 2, 5).reshape(-1)          # [e,t,s,j,r,c]
 
@@ -92,8 +92,9 @@ def test_weight_pack_is_a_permutation(elem):
     wp, _ = oracle.pack_weights(elem, ROW32, E, N, K, std.reshape(E, N, kb), codes)
     np.testing.assert_array_equal(wp, std[perm])
     np.testing.assert_array_equal(wp[inv], std)
-    # lane ownership: lane l = 16 j + r of chunk (t, s) reads row 16 t + r,
-    # K values 128 s + 32 j .. + 32, as 16-byte pieces at 16 l (+ 1024)
+    # lane ownership: lane l = 16 j + r of chunk (t, s) reads row 16 t + r as
+    # 16-byte pieces at 16 l (+ 1024): e4m3 K 16 j.. and 64 + 16 j.. of the
+    # step, e2m1 the 32-value block j of the step
     S, T = K // 128, N // 16
     for (e, t, s, l) in [(0, 0, 0, 0), (1, 1, 1, 63), (0, 1, 0, 17), (1, 0, 1, 40)]:
         r, j = l % 16, l // 16
@@ -101,7 +102,9 @@ def test_weight_pack_is_a_permutation(elem):
         if elem == E4M3:
             got = np.concatenate([wp[base + 16 * l: base + 16 * l + 16],
                                   wp[base + 1024 + 16 * l: base + 1024 + 16 * l + 16]])
-            want = std.reshape(E, N, K)[e, 16 * t + r, 128 * s + 32 * j: 128 * s + 32 * j + 32]
+            row = std.reshape(E, N, K)[e, 16 * t + r]
+            want = np.concatenate([row[128 * s + 16 * j: 128 * s + 16 * j + 16],
+                                   row[128 * s + 64 + 16 * j: 128 * s + 64 + 16 * j + 16]])
         else:
             got = wp[base + 16 * l: base + 16 * l + 16]
             want = std.reshape(E, N, K // 2)[e, 16 * t + r, 64 * s + 16 * j: 64 * s + 16 * j + 16]
