@@ -1,0 +1,187 @@
+/*
+ * mx.h -- C ABI of libmx: the block-scaled (OCP microscaling, "MX") linear
+ * layer y = x . W^T on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *   [weights942]   vllm.models.deepseek_v41.amd.mono.weights942
+ *   [rocm_native]  vllm.model_executor.kernels.linear.mxfp8.rocm_native
+ *   [a16w4]        vllm.models.minimax_m3.amd.specialized_decode.mono.a16w4
+ *
+ * Number formats.
+ *   E4M3   OCP fp8 byte (bias 7, max 448, 0x7F/0xFF NaN)        [weights942]
+ *   E2M1   OCP fp4 nibble, two per byte, low nibble = even K       [a16w4] dequant
+ *   E8M0   scale code c meaning 2^(c - 127), 255 = NaN            [weights942] ocp_from_dequant
+ *   bf16   activations, bias and outputs
+ * Every 32 consecutive K values of a weight row share one E8M0 code, laid out
+ * either one code per row and block (ROW32, [E*N, K/32]) or one code per
+ * 32 rows x 32 K block (BLK32, [E*N/32, K/32]) ([rocm_native]
+ * process_weights_after_loading and _as_block32_scale).
+ *
+ * Conventions for every entry point.
+ *   - Pointers marked (device) are device memory of the current HIP device;
+ *     (host) are host memory.  The caller allocates and owns every buffer;
+ *     the library never allocates device memory in these calls.
+ *   - All device work is enqueued on `stream` (0 = the null stream) and the
+ *     calls return without synchronizing, except mx_pack_weights (below).
+ *   - Arguments are validated on the host before anything is launched; on an
+ *     error nothing is launched and outputs are untouched.
+ *   - Each call checks that the current device is gfx950 (MX_ERR_DEVICE).
+ *   - Inputs holding NaN or Inf give unspecified outputs.
+ */
+#ifndef MX_H
+#define MX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t *mx_stream_t; /* same type as hipStream_t */
+
+typedef enum {
+    MX_OK = 0,
+    MX_ERR_NULL = 1,        /* a required pointer is NULL                      */
+    MX_ERR_SHAPE = 2,       /* a size or leading dimension breaks the rules    */
+    MX_ERR_ALIGN = 3,       /* a pointer or leading dimension is misaligned    */
+    MX_ERR_VALUE = 4,       /* an E8M0 weight code 255 (NaN) was found at pack */
+    MX_ERR_UNSUPPORTED = 5, /* a format / layout / mode combination not built  */
+    MX_ERR_DEVICE = 6,      /* the current device is not gfx950 (or none)     */
+    MX_ERR_WORKSPACE = 7,   /* the workspace is NULL or smaller than required  */
+    MX_ERR_LAUNCH = 8       /* a HIP call or kernel launch failed              */
+} mx_status;
+
+typedef enum { MX_E4M3 = 0, MX_E2M1 = 1 } mx_elem;
+typedef enum { MX_SCALE_ROW32 = 0, MX_SCALE_BLK32 = 1 } mx_scale_layout;
+/* Activation scale rules ([rocm_native] _quant_mxfp8_tile and OCP MX v1.0):
+ *   MX_RULE_OCP      code = clamp(floor(log2 amax) - 8 + 127, 0, 254); the
+ *                    scaled elements are rounded to nearest-even e4m3 and
+ *                    saturated to +-448.
+ *   MX_RULE_CEIL448  code = clamp(ceil(log2(max(amax, 2^-126) / 448)) + 127,
+ *                    0, 254); the scaled elements never exceed 448.
+ * Either way a block whose amax is 0 gets code 0, and a zero element keeps
+ * its sign (-0 -> 0x80). */
+typedef enum { MX_RULE_OCP = 0, MX_RULE_CEIL448 = 1 } mx_quant_rule;
+/* MX_ACT_BF16: activations stay bf16 (A16W8 / A16W4).
+ * MX_ACT_MXFP8: activations are MXFP8, e4m3 bytes [M, K] with row-major
+ * E8M0 codes [M, K/32] ([rocm_native] input_quant_key: row-major, not
+ * swizzled), either given pre-quantized or quantized inside the call (W8A8). */
+typedef enum { MX_ACT_BF16 = 0, MX_ACT_MXFP8 = 1 } mx_act;
+
+/*
+ * Packed weight layout ("W-T16", [weights942] dense_copy / fp4_tile_major
+ * tile-major idea; [a16w4] module notes for E2M1).
+ *   Kp = K rounded up to a multiple of 128 (zero bytes; padded blocks get code
+ *   128, [weights942] dense_copy), S = Kp / 128 steps, T = N / 16 tiles,
+ *   Q = ceil(S / 4).  Lane l = 16 j + r.
+ *   E4M3: chunk (e, t, s) of 2048 bytes at ((e T + t) S + s) * 2048;
+ *         byte 1024 h + 16 l + c = W[e][16 t + r][128 s + 64 h + 16 j + c].
+ *   E2M1: chunk (e, t, s) of 1024 bytes at ((e T + t) S + s) * 1024;
+ *         byte 16 l + c = packed byte 64 s + 16 j + c of row 16 t + r.
+ * Packed codes:
+ *   ROW32: 256 bytes per (e, t, q) at ((e T + t) Q + q) * 256;
+ *          byte 4 l + u = code[e N + 16 t + r][4 (4 q + u) + j].
+ *   BLK32: row-major [E N / 32, Kp / 32].
+ */
+
+/* Sizes of the packed buffers for a weight of E experts x [N, K].
+ * Rules: E >= 1, K >= 32 and K % 32 == 0, N % 16 == 0 (N % 32 == 0 for
+ * BLK32).  w_bytes, code_bytes (host) receive the sizes.
+ * Errors: MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_UNSUPPORTED (unknown enum). */
+mx_status mx_packed_sizes(int elem, int layout, int64_t E, int64_t N, int64_t K,
+                          size_t *w_bytes, size_t *code_bytes);
+
+/* Load-time repack ([weights942] dense_copy, fp4_tile_major,
+ * codes_tile_rounds; [rocm_native] process_weights_after_loading).
+ *   w      (device) standard weight bytes: E4M3 [E, N, K], E2M1 [E, N, K/2]
+ *   codes  (device) ROW32 [E N, K/32] or BLK32 [E N / 32, K / 32]
+ *   w_packed, codes_packed (device) outputs of mx_packed_sizes' sizes
+ *   ws     (device) at least 256 bytes of scratch
+ * All device pointers 16-byte aligned.  This call synchronizes `stream`: it
+ * reads back whether any code is 255 and returns MX_ERR_VALUE if so (the
+ * packed outputs are then written but must not be used). */
+mx_status mx_pack_weights(int elem, int layout, int64_t E, int64_t N, int64_t K,
+                          const void *w, const void *codes, void *w_packed,
+                          void *codes_packed, void *ws, size_t ws_bytes,
+                          mx_stream_t stream);
+
+/* Per-token MXFP8 activation quantization ([rocm_native] _quant_mxfp8_tile;
+ * rule as in mx_quant_rule).
+ *   x      (device) bf16 [M, ldx], 16-byte aligned, ldx % 8 == 0, ldx >= K
+ *   xq     (device) e4m3 [M, ldq], 16-byte aligned, ldq % 16 == 0, ldq >= K
+ *   xcodes (device) E8M0 [M, ldc], ldc >= K / 32
+ * Rules: M >= 1, K >= 32, K % 32 == 0.  Bytes and codes are bit-exact with
+ * the rule's definition. */
+mx_status mx_quant_act(int64_t M, int64_t K, const void *x, int64_t ldx,
+                       void *xq, int64_t ldq, void *xcodes, int64_t ldc,
+                       int rule, mx_stream_t stream);
+
+/* Workspace bytes mx_linear needs for these arguments (0 when none):
+ * M * Kp + M * Kp / 32 (+ alignment) when act == MX_ACT_MXFP8 and the
+ * activation is quantized inside the call (pass prequantized = 0). */
+mx_status mx_linear_workspace(int elem, int layout, int64_t N, int64_t K,
+                              int64_t M, int act, int prequantized,
+                              size_t *bytes);
+
+/* y[M, N] = a . Wf^T (+ bias), bf16 out, fp32 accumulation, one final
+ * round to nearest-even bf16 ([rocm_native] apply_weights).
+ *   Wf[n][k] = dec(W[n][k]) * 2^(code(n, k) - 127) from the packed buffers.
+ *   a = x (bf16) when act == MX_ACT_BF16;
+ *   a = dec(xq) * 2^(xcode - 127) when act == MX_ACT_MXFP8: if xq and xcodes
+ *       are both non-NULL they are used as given (pre-quantized, row-major
+ *       codes); otherwise x is quantized first with `rule` into ws.
+ *   w_packed, codes_packed (device) from mx_pack_weights with the same
+ *       elem, layout, E = 1, N, K.
+ *   x   (device) bf16 [M, ldx]: 16-byte aligned, ldx % 8 == 0, ldx >= K
+ *   xq  (device) e4m3 [M, ldq]: 16-byte aligned, ldq % 16 == 0, ldq >= K
+ *   xcodes (device) [M, ldc], ldc >= K / 32
+ *   bias (device, nullable) bf16 [N]
+ *   y   (device) bf16 [M, ldy]: 16-byte aligned, ldy % 8 == 0, ldy >= N
+ * Built combinations: E4M3 x {ROW32, BLK32} x {BF16, MXFP8};
+ * E2M1 x ROW32 x BF16.  Others: MX_ERR_UNSUPPORTED. */
+mx_status mx_linear(int elem, int layout, int64_t N, int64_t K,
+                    const void *w_packed, const void *codes_packed, int64_t M,
+                    int act, int rule, const void *x, int64_t ldx,
+                    const void *xq, int64_t ldq, const void *xcodes,
+                    int64_t ldc, const void *bias, void *y, int64_t ldy,
+                    void *ws, size_t ws_bytes, mx_stream_t stream);
+
+/* Workspace bytes mx_moe_linear needs: T * topk * N * 4 when topk_weights is
+ * used (combine mode), else 0. */
+mx_status mx_moe_workspace(int elem, int64_t E, int64_t N, int64_t K,
+                           int64_t T, int64_t topk, int combine,
+                           size_t *bytes);
+
+/* Grouped MoE linear over routed experts ([weights942] moe_copies: expert
+ * tensors [E, N, K(/2)] with codes [E N, K/32]; [a16w4] module notes):
+ *   per slot (topk_weights == NULL): y[t][k][:] = x[t] . Wf[id[t][k]]^T,
+ *       y bf16 [T, topk, N] contiguous;
+ *   combined (topk_weights != NULL): y[t][:] = sum_k w[t][k] y_slot[t][k][:]
+ *       summed in k order in fp32, y bf16 [T, N] contiguous.
+ *   w_packed, codes_packed (device) from mx_pack_weights(elem, ROW32, E, N, K)
+ *   x (device) bf16 [T, ldx], 16-byte aligned, ldx % 8 == 0, ldx >= K
+ *   topk_ids (device) int32 [T, topk]; an id outside [0, E) gives a zero row
+ *   topk_weights (device, nullable) fp32 [T, topk]
+ * Rules: T >= 1, 1 <= topk <= E, T * topk <= 4096.  Experts that receive no
+ * token read no weight bytes.  Built: E2M1 and E4M3 weights, bf16 x. */
+mx_status mx_moe_linear(int elem, int64_t E, int64_t N, int64_t K,
+                        const void *w_packed, const void *codes_packed,
+                        int64_t T, int64_t topk, const void *x, int64_t ldx,
+                        const int32_t *topk_ids, const float *topk_weights,
+                        void *y, void *ws, size_t ws_bytes,
+                        mx_stream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char *mx_status_str(mx_status status);
+
+/* Whether an architecture name (e.g. "gfx950:sramecc+:xnack-") is one the
+ * kernels are built for; the same test every entry point applies to the
+ * current device.  Host only, no device access. */
+int mx_arch_supported(const char *gcn_arch_name);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MX_H */

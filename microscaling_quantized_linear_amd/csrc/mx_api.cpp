@@ -1,0 +1,308 @@
+// mx_api.cpp -- the C ABI of libmx (include/mx.h): host-side validation,
+// the gfx950 gate, workspace sizing and dispatch to the kernels.
+//
+// Validation is pure host code and runs before any device call, so every
+// error path can be exercised without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/mx.h"
+#include "mx_kernels.h"
+
+namespace {
+
+using mx::ACT_BF16;
+using mx::ACT_MXFP8;
+using mx::BLK32;
+using mx::E2M1;
+using mx::E4M3;
+using mx::ROW32;
+
+constexpr int64_t kMaxRsrc = (int64_t(1) << 31) - 1;   // 32-bit buffer offsets
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int64_t padded_k(int64_t K) { return (K + 127) / 128 * 128; }
+
+mx_status shape_ok(int elem, int layout, int64_t E, int64_t N, int64_t K) {
+    if (elem != E4M3 && elem != E2M1) return MX_ERR_UNSUPPORTED;
+    if (layout != ROW32 && layout != BLK32) return MX_ERR_UNSUPPORTED;
+    if (E < 1 || N < 16 || K < 32 || K % 32 != 0 || N % 16 != 0) return MX_ERR_SHAPE;
+    if (layout == BLK32 && N % 32 != 0) return MX_ERR_SHAPE;
+    return MX_OK;
+}
+
+// -1 unknown, 0 unsupported, 1 gfx950; one entry per device ordinal
+std::atomic<int> g_arch[64];
+struct ArchInit {
+    ArchInit() {
+        for (auto &a : g_arch) a.store(-1);
+    }
+} g_arch_init;
+
+mx_status device_ok() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MX_ERR_DEVICE;
+    if (dev < 64) {
+        int v = g_arch[dev].load();
+        if (v >= 0) return v ? MX_OK : MX_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MX_ERR_DEVICE;
+    const int ok = mx_arch_supported(prop.gcnArchName);
+    if (dev < 64) g_arch[dev].store(ok);
+    return ok ? MX_OK : MX_ERR_DEVICE;
+}
+
+mx_status launched(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH; }
+
+// waves per GEMV workgroup; MX_GEMV_WAVES (1, 2, 4, 8) overrides, read once
+int gemv_waves(int64_t S) {
+    static const int forced = [] {
+        const char *s = std::getenv("MX_GEMV_WAVES");
+        const int v = s ? std::atoi(s) : 0;
+        return (v == 1 || v == 2 || v == 4 || v == 8) ? v : 0;
+    }();
+    if (forced) return forced;
+    if (S >= 32) return 8;
+    if (S >= 8) return 4;
+    return S >= 2 ? 2 : 1;
+}
+
+// largest M served by the decode GEMV for W8A8; above it the GEMM runs
+constexpr int64_t kGemvMaxM = 64;
+
+}  // namespace
+
+extern "C" {
+
+const char *mx_status_str(mx_status s) {
+    switch (s) {
+    case MX_OK: return "ok";
+    case MX_ERR_NULL: return "a required pointer is NULL";
+    case MX_ERR_SHAPE: return "a size or leading dimension breaks the layout rules";
+    case MX_ERR_ALIGN: return "a pointer or leading dimension is misaligned";
+    case MX_ERR_VALUE: return "an E8M0 weight code is 255 (NaN)";
+    case MX_ERR_UNSUPPORTED: return "format / layout / activation combination not built";
+    case MX_ERR_DEVICE: return "the current device is not gfx950";
+    case MX_ERR_WORKSPACE: return "workspace missing or too small";
+    case MX_ERR_LAUNCH: return "a HIP call or kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int mx_arch_supported(const char *name) {
+    if (!name) return 0;
+    return std::strncmp(name, "gfx950", 6) == 0 && (name[6] == '\0' || name[6] == ':');
+}
+
+mx_status mx_packed_sizes(int elem, int layout, int64_t E, int64_t N, int64_t K,
+                          size_t *w_bytes, size_t *code_bytes) {
+    if (!w_bytes || !code_bytes) return MX_ERR_NULL;
+    mx_status st = shape_ok(elem, layout, E, N, K);
+    if (st != MX_OK) return st;
+    const int64_t Kp = padded_k(K), S = Kp / 128, Q = (S + 3) / 4;
+    *w_bytes = (size_t)(E * N * (elem == E4M3 ? Kp : Kp / 2));
+    *code_bytes = (size_t)(layout == ROW32 ? E * (N / 16) * Q * 256 : E * (N / 32) * (Kp / 32));
+    return MX_OK;
+}
+
+mx_status mx_pack_weights(int elem, int layout, int64_t E, int64_t N, int64_t K, const void *w,
+                          const void *codes, void *w_packed, void *codes_packed, void *ws,
+                          size_t ws_bytes, mx_stream_t stream) {
+    size_t wb, cb;
+    mx_status st = mx_packed_sizes(elem, layout, E, N, K, &wb, &cb);
+    if (st != MX_OK) return st;
+    if (!w || !codes || !w_packed || !codes_packed || !ws) return MX_ERR_NULL;
+    if (!aligned16(w) || !aligned16(codes) || !aligned16(w_packed) || !aligned16(codes_packed) ||
+        !aligned16(ws))
+        return MX_ERR_ALIGN;
+    if (ws_bytes < 256) return MX_ERR_WORKSPACE;
+    if ((st = device_ok()) != MX_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    int *bad = static_cast<int *>(ws);
+    if (hipMemsetAsync(bad, 0, sizeof(int), s) != hipSuccess) return MX_ERR_LAUNCH;
+    if ((st = launched(mx::launch_pack(elem, layout, E, N, K, w, codes, w_packed, codes_packed,
+                                       bad, s))) != MX_OK)
+        return st;
+    int h = 0;
+    if (hipMemcpyAsync(&h, bad, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return MX_ERR_LAUNCH;
+    return h ? MX_ERR_VALUE : MX_OK;
+}
+
+mx_status mx_quant_act(int64_t M, int64_t K, const void *x, int64_t ldx, void *xq, int64_t ldq,
+                       void *xcodes, int64_t ldc, int rule, mx_stream_t stream) {
+    if (rule != mx::RULE_OCP && rule != mx::RULE_CEIL448) return MX_ERR_UNSUPPORTED;
+    if (M < 1 || K < 32 || K % 32 != 0 || ldx < K || ldq < K || ldc < K / 32) return MX_ERR_SHAPE;
+    if (!x || !xq || !xcodes) return MX_ERR_NULL;
+    if (!aligned16(x) || !aligned16(xq) || ldx % 8 != 0 || ldq % 16 != 0) return MX_ERR_ALIGN;
+    mx_status st = device_ok();
+    if (st != MX_OK) return st;
+    return launched(mx::launch_quant(M, K, x, ldx, xq, ldq, xcodes, ldc, rule,
+                                     reinterpret_cast<hipStream_t>(stream)));
+}
+
+mx_status mx_linear_workspace(int elem, int layout, int64_t N, int64_t K, int64_t M, int act,
+                              int prequantized, size_t *bytes) {
+    if (!bytes) return MX_ERR_NULL;
+    mx_status st = shape_ok(elem, layout, 1, N, K);
+    if (st != MX_OK) return st;
+    if (M < 1) return MX_ERR_SHAPE;
+    if (act != ACT_BF16 && act != ACT_MXFP8) return MX_ERR_UNSUPPORTED;
+    *bytes = 0;
+    if (act == ACT_MXFP8 && !prequantized) {
+        const int64_t Kp = padded_k(K);
+        *bytes = (size_t)(M * Kp + 256 + M * (Kp / 32));
+    }
+    return MX_OK;
+}
+
+mx_status mx_linear(int elem, int layout, int64_t N, int64_t K, const void *w_packed,
+                    const void *codes_packed, int64_t M, int act, int rule, const void *x,
+                    int64_t ldx, const void *xq, int64_t ldq, const void *xcodes, int64_t ldc,
+                    const void *bias, void *y, int64_t ldy, void *ws, size_t ws_bytes,
+                    mx_stream_t stream) {
+    mx_status st = shape_ok(elem, layout, 1, N, K);
+    if (st != MX_OK) return st;
+    if (act != ACT_BF16 && act != ACT_MXFP8) return MX_ERR_UNSUPPORTED;
+    if (rule != mx::RULE_OCP && rule != mx::RULE_CEIL448) return MX_ERR_UNSUPPORTED;
+    if (elem == E2M1 && (layout != ROW32 || act != ACT_BF16)) return MX_ERR_UNSUPPORTED;
+    if (M < 1 || ldy < N) return MX_ERR_SHAPE;
+    if (!w_packed || !codes_packed || !y) return MX_ERR_NULL;
+    if (!aligned16(w_packed) || !aligned16(codes_packed) || !aligned16(y) || ldy % 8 != 0)
+        return MX_ERR_ALIGN;
+    if (bias && (reinterpret_cast<uintptr_t>(bias) & 1u)) return MX_ERR_ALIGN;
+    const int64_t Kp = padded_k(K);
+    const bool preq = act == ACT_MXFP8 && xq && xcodes;
+    if (act == ACT_BF16 || !preq) {
+        if (!x) return MX_ERR_NULL;
+        if (ldx < K) return MX_ERR_SHAPE;
+        if (!aligned16(x) || ldx % 8 != 0) return MX_ERR_ALIGN;
+        if (M * ldx * 2 > kMaxRsrc) return MX_ERR_SHAPE;
+    }
+    if (preq) {
+        if (ldq < K || ldc < K / 32) return MX_ERR_SHAPE;
+        if (!aligned16(xq) || ldq % 16 != 0) return MX_ERR_ALIGN;
+        if (M * ldq > kMaxRsrc || M * ldc > kMaxRsrc) return MX_ERR_SHAPE;
+    }
+    size_t need = 0;
+    mx_linear_workspace(elem, layout, N, K, M, act, preq ? 1 : 0, &need);
+    if (need > 0 && (!ws || ws_bytes < need)) return MX_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(ws)) return MX_ERR_ALIGN;
+    const bool gemm = act == ACT_MXFP8 && M > kGemvMaxM;
+    if (gemm && N * Kp > kMaxRsrc) return MX_ERR_SHAPE;
+    if ((st = device_ok()) != MX_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+    const uint8_t *aq = static_cast<const uint8_t *>(xq);
+    const uint8_t *ac = static_cast<const uint8_t *>(xcodes);
+    int64_t lq = ldq, lc = ldc;
+    if (act == ACT_MXFP8 && !preq) {
+        // quantize into the workspace: e4m3 [M, Kp] then codes [M, Kp/32]
+        uint8_t *q = static_cast<uint8_t *>(ws);
+        uint8_t *c = q + ((M * Kp + 255) / 256) * 256;
+        lq = Kp;
+        lc = Kp / 32;
+        if ((st = launched(mx::launch_quant(M, K, x, ldx, q, lq, c, lc, rule, s))) != MX_OK)
+            return st;
+        aq = q;
+        ac = c;
+    }
+    if (gemm) {
+        mx::GemmArgs g{};
+        g.w = static_cast<const uint8_t *>(w_packed);
+        g.codes = static_cast<const uint8_t *>(codes_packed);
+        g.N = N;
+        g.K = K;
+        g.M = M;
+        g.xq = aq;
+        g.ldq = lq;
+        g.xcodes = ac;
+        g.ldc = lc;
+        g.bias = static_cast<const uint16_t *>(bias);
+        g.y = static_cast<uint16_t *>(y);
+        g.ldy = ldy;
+        return launched(mx::launch_gemm(layout, g, s));
+    }
+    mx::GemvArgs a{};
+    a.w = static_cast<const uint8_t *>(w_packed);
+    a.codes = static_cast<const uint8_t *>(codes_packed);
+    a.E = 1;
+    a.N = N;
+    a.K = K;
+    a.rows = M;
+    a.topk = 1;
+    a.xrows = M;
+    if (act == ACT_MXFP8) {
+        a.x = aq;
+        a.ldx = lq;
+        a.xcodes = ac;
+        a.ldc = lc;
+    } else {
+        a.x = x;
+        a.ldx = ldx;
+    }
+    a.bias = static_cast<const uint16_t *>(bias);
+    a.y = static_cast<uint16_t *>(y);
+    a.ldy = ldy;
+    return launched(mx::launch_gemv(elem, layout, act, false, a, gemv_waves(Kp / 128), s));
+}
+
+mx_status mx_moe_workspace(int elem, int64_t E, int64_t N, int64_t K, int64_t T, int64_t topk,
+                           int combine, size_t *bytes) {
+    if (!bytes) return MX_ERR_NULL;
+    mx_status st = shape_ok(elem, ROW32, E, N, K);
+    if (st != MX_OK) return st;
+    if (T < 1 || topk < 1 || topk > E || T * topk > mx::kMoeMaxPairs) return MX_ERR_SHAPE;
+    *bytes = combine ? (size_t)(T * topk * N * 4) : 0;
+    return MX_OK;
+}
+
+mx_status mx_moe_linear(int elem, int64_t E, int64_t N, int64_t K, const void *w_packed,
+                        const void *codes_packed, int64_t T, int64_t topk, const void *x,
+                        int64_t ldx, const int32_t *topk_ids, const float *topk_weights, void *y,
+                        void *ws, size_t ws_bytes, mx_stream_t stream) {
+    size_t need = 0;
+    mx_status st = mx_moe_workspace(elem, E, N, K, T, topk, topk_weights ? 1 : 0, &need);
+    if (st != MX_OK) return st;
+    if (ldx < K) return MX_ERR_SHAPE;
+    if (T * ldx * 2 > kMaxRsrc) return MX_ERR_SHAPE;
+    if (!w_packed || !codes_packed || !x || !topk_ids || !y) return MX_ERR_NULL;
+    if (!aligned16(w_packed) || !aligned16(codes_packed) || !aligned16(x) || !aligned16(y) ||
+        ldx % 8 != 0 || (reinterpret_cast<uintptr_t>(topk_ids) & 3u) ||
+        (topk_weights && (reinterpret_cast<uintptr_t>(topk_weights) & 3u)))
+        return MX_ERR_ALIGN;
+    if (need > 0 && (!ws || ws_bytes < need)) return MX_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(ws)) return MX_ERR_ALIGN;
+    if ((st = device_ok()) != MX_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int64_t Kp = padded_k(K);
+    mx::GemvArgs a{};
+    a.w = static_cast<const uint8_t *>(w_packed);
+    a.codes = static_cast<const uint8_t *>(codes_packed);
+    a.E = E;
+    a.N = N;
+    a.K = K;
+    a.rows = T;
+    a.topk = topk;
+    a.xrows = T;
+    a.x = x;
+    a.ldx = ldx;
+    a.ids = topk_ids;
+    a.y = static_cast<uint16_t *>(y);
+    a.ldy = N;
+    a.ws = topk_weights ? static_cast<float *>(ws) : nullptr;
+    const int nw = gemv_waves(Kp / 128) > 4 ? 4 : gemv_waves(Kp / 128);
+    if ((st = launched(mx::launch_gemv(elem, ROW32, ACT_BF16, true, a, nw, s))) != MX_OK)
+        return st;
+    if (topk_weights)
+        return launched(mx::launch_moe_combine(T, topk, N, static_cast<const float *>(ws),
+                                               topk_weights, y, s));
+    return MX_OK;
+}
+
+}  // extern "C"

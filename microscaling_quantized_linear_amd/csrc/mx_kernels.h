@@ -1,0 +1,59 @@
+// mx_kernels.h -- internal interface between the host dispatcher (mx_api.cpp)
+// and the gfx950 kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+// the enum values of include/mx.h
+enum { E4M3 = 0, E2M1 = 1 };
+enum { ROW32 = 0, BLK32 = 1 };
+enum { RULE_OCP = 0, RULE_CEIL448 = 1 };
+enum { ACT_BF16 = 0, ACT_MXFP8 = 1 };
+
+constexpr int kMoeMaxPairs = 4096;   // T * topk handled by one routing scan
+
+struct GemvArgs {
+    const uint8_t *w;        // packed W-T16 weights (all experts)
+    const uint8_t *codes;    // packed codes
+    int64_t E, N, K;
+    int64_t rows;            // dense: M tokens; MoE: T tokens
+    int64_t topk;            // MoE only
+    int64_t xrows;           // rows of the activation buffer
+    const void *x;           // bf16 [xrows, ldx] or e4m3 [xrows, ldx]
+    int64_t ldx;             // elements
+    const uint8_t *xcodes;   // MXFP8 codes [xrows, ldc]
+    int64_t ldc;
+    const int32_t *ids;      // MoE routing [T, topk]
+    const uint16_t *bias;    // bf16 [N] or null
+    uint16_t *y;             // bf16 output
+    int64_t ldy;
+    float *ws;               // MoE combine mode: fp32 per-slot rows [T*topk, N]
+};
+
+struct GemmArgs {
+    const uint8_t *w, *codes;
+    int64_t N, K, M;
+    const uint8_t *xq;
+    int64_t ldq;
+    const uint8_t *xcodes;
+    int64_t ldc;
+    const uint16_t *bias;
+    uint16_t *y;
+    int64_t ldy;
+};
+
+hipError_t launch_pack(int elem, int layout, int64_t E, int64_t N, int64_t K, const void *w,
+                       const void *codes, void *wp, void *cp, int *bad, hipStream_t stream);
+hipError_t launch_quant(int64_t M, int64_t K, const void *x, int64_t ldx, void *xq, int64_t ldq,
+                        void *xcodes, int64_t ldc, int rule, hipStream_t stream);
+hipError_t launch_gemv(int elem, int layout, int act, bool moe, const GemvArgs &a, int nw,
+                       hipStream_t stream);
+hipError_t launch_moe_combine(int64_t T, int64_t topk, int64_t N, const float *ys,
+                              const float *wts, void *y, hipStream_t stream);
+hipError_t launch_gemm(int layout, const GemmArgs &a, hipStream_t stream);
+int gemm_tile_n(int64_t N);
+
+}  // namespace mx

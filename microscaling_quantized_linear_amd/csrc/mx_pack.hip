@@ -1,0 +1,100 @@
+// mx_pack.hip -- load-time repacks into the W-T16 weight layout and the
+// C-T16 / padded BLK32 code layouts (layouts stated in include/mx.h).
+//
+// The tile-major weight copy follows the idea of [weights942] dense_copy and
+// fp4_tile_major (16-row tiles x 128-K steps, each 16-byte load of a
+// wavefront reading 1 KB that is contiguous); the code staging follows
+// [weights942] codes_tile_rounds (a lane group reads its rows' codes from one
+// line) with the per-lane dwords of [a16w4] scale_loads.  Padding to
+// Kp = 128 * ceil(K / 128) uses zero bytes and code 128 ([weights942]
+// dense_copy).
+#include "mx_device.h"
+#include "mx_kernels.h"
+
+namespace mx {
+
+// One thread writes one 16-byte piece of the packed weights (a gather: every
+// destination piece is read from exactly one source piece, or zero-filled).
+__global__ void __launch_bounds__(256) pack_weights_kernel(
+    int elem, int64_t E, int64_t N, int64_t K, const uint8_t *__restrict__ w,
+    uint8_t *__restrict__ wp, int64_t npieces) {
+    int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= npieces) return;
+    const int64_t Kp = (K + 127) / 128 * 128, S = Kp / 128, T = N / 16;
+    const int64_t row_bytes = elem == E4M3 ? K : K / 2;
+    int64_t chunk, lane, h, kbyte;
+    if (elem == E4M3) {             // 128 pieces per 2 KB chunk
+        chunk = p / 128;
+        h = (p % 128) / 64;
+        lane = p % 64;
+        kbyte = 64 * h + 16 * (lane / 16);
+    } else {                        // 64 pieces per 1 KB chunk
+        chunk = p / 64;
+        lane = p % 64;
+        kbyte = 16 * (lane / 16);
+    }
+    const int64_t s = chunk % S, et = chunk / S;          // et = e * T + t
+    const int64_t e = et / T, t = et % T;
+    const int64_t row = e * N + 16 * t + lane % 16;
+    const int64_t step_bytes = elem == E4M3 ? 128 : 64;
+    const int64_t off = s * step_bytes + kbyte;           // byte within the row
+    v4u v = {0u, 0u, 0u, 0u};
+    if (off < row_bytes)                                   // K % 32 == 0: whole piece in or out
+        v = *reinterpret_cast<const v4u *>(w + row * row_bytes + off);
+    *reinterpret_cast<v4u *>(wp + p * 16) = v;
+}
+
+// ROW32: one thread writes one dword (4 codes) of C-T16.  BLK32: one byte.
+// Any code 255 sets *bad.
+__global__ void __launch_bounds__(256) pack_codes_kernel(
+    int layout, int64_t E, int64_t N, int64_t K, const uint8_t *__restrict__ codes,
+    uint8_t *__restrict__ cp, int64_t nunits, int *__restrict__ bad) {
+    int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= nunits) return;
+    const int64_t KB = K / 32, Kp = (K + 127) / 128 * 128, S = Kp / 128, Q = (S + 3) / 4;
+    const int64_t T = N / 16;
+    int found = 0;
+    if (layout == ROW32) {
+        const int64_t lane = p % 64, etq = p / 64;
+        const int64_t q = etq % Q, et = etq / Q;
+        const int64_t row = (et / T) * N + 16 * (et % T) + lane % 16;
+        uint32_t dw = 0;
+        for (int u = 0; u < 4; ++u) {
+            const int64_t blk = 4 * (4 * q + u) + lane / 16;
+            uint32_t c = 128;
+            if (blk < KB) {
+                c = codes[row * KB + blk];
+                found |= c == 255;
+            }
+            dw |= c << (8 * u);
+        }
+        reinterpret_cast<uint32_t *>(cp)[p] = dw;
+    } else {
+        const int64_t R = p / (Kp / 32), b = p % (Kp / 32);
+        uint32_t c = 128;
+        if (b < KB) {
+            c = codes[R * KB + b];
+            found = c == 255;
+        }
+        cp[p] = (uint8_t)c;
+    }
+    if (found) atomicOr(bad, 1);
+}
+
+hipError_t launch_pack(int elem, int layout, int64_t E, int64_t N, int64_t K, const void *w,
+                       const void *codes, void *wp, void *cp, int *bad, hipStream_t stream) {
+    const int64_t Kp = (K + 127) / 128 * 128, S = Kp / 128, Q = (S + 3) / 4;
+    const int64_t wbytes = E * N * (elem == E4M3 ? Kp : Kp / 2);
+    const int64_t npieces = wbytes / 16;
+    hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)((npieces + 255) / 256)), dim3(256), 0,
+                       stream, elem, E, N, K, (const uint8_t *)w, (uint8_t *)wp, npieces);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t nunits = layout == ROW32 ? E * (N / 16) * Q * 64 : E * (N / 32) * (Kp / 32);
+    hipLaunchKernelGGL(pack_codes_kernel, dim3((unsigned)((nunits + 255) / 256)), dim3(256), 0,
+                       stream, layout, E, N, K, (const uint8_t *)codes, (uint8_t *)cp, nunits,
+                       bad);
+    return hipGetLastError();
+}
+
+}  // namespace mx

@@ -1,0 +1,145 @@
+"""CPU-side tests of libmx: the library loads, exports every entry point that
+include/mx.h declares, sizes packed buffers like the oracle's layout
+definition, and rejects bad arguments with the documented status before any
+device work (no GPU is needed for any of these)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import microscaling_quantized_linear_amd as mx
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, NULL, SHAPE, ALIGN, VALUE, UNSUP, DEVICE, WS, LAUNCH = range(9)
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "mx.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:mx_status|const char \*|int)\s*\**\s*(mx_\w+)\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert {"mx_pack_weights", "mx_quant_act", "mx_linear", "mx_moe_linear"} <= set(names)
+    L = mx.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for s in range(9):
+        assert mx.mx_status_str(s)
+    assert mx.mx_status_str(77) == "unknown status"
+
+
+def test_arch_gate_strings():
+    assert mx.mx_arch_supported("gfx950")
+    assert mx.mx_arch_supported("gfx950:sramecc+:xnack-")
+    for bad in ("gfx942", "gfx942:sramecc+:xnack-", "gfx9500", "gfx90a", "", "sm_90"):
+        assert not mx.mx_arch_supported(bad)
+
+
+@pytest.mark.parametrize("elem,layout,E,N,K", [
+    (0, 0, 1, 256, 512), (0, 1, 1, 7168, 7168), (0, 0, 1, 4096, 1568),
+    (1, 0, 32, 3072, 3072), (1, 0, 2, 16, 160), (0, 1, 3, 64, 96)])
+def test_packed_sizes_match_oracle_layout(elem, layout, E, N, K):
+    assert mx.mx_packed_sizes(elem, layout, E, N, K) == oracle.packed_sizes(elem, layout, E, N, K)
+
+
+def _status(fn, *args):
+    return getattr(mx.lib(), fn)(*args)
+
+
+def test_shape_and_enum_errors():
+    wb, cb = C.c_size_t(), C.c_size_t()
+    L = mx.lib()
+    assert L.mx_packed_sizes(0, 0, 1, 24, 512, C.byref(wb), C.byref(cb)) == SHAPE
+    assert L.mx_packed_sizes(0, 1, 1, 48, 512, C.byref(wb), C.byref(cb)) == SHAPE
+    assert L.mx_packed_sizes(0, 0, 1, 32, 100, C.byref(wb), C.byref(cb)) == SHAPE
+    assert L.mx_packed_sizes(0, 0, 0, 32, 128, C.byref(wb), C.byref(cb)) == SHAPE
+    assert L.mx_packed_sizes(2, 0, 1, 32, 128, C.byref(wb), C.byref(cb)) == UNSUP
+    assert L.mx_packed_sizes(0, 5, 1, 32, 128, C.byref(wb), C.byref(cb)) == UNSUP
+    assert L.mx_packed_sizes(0, 0, 1, 32, 128, None, C.byref(cb)) == NULL
+
+
+A = 1 << 20          # fake, 16-byte aligned "device" addresses: never dereferenced
+
+
+def _linear(**kw):
+    a = dict(elem=0, layout=0, N=64, K=256, w=A, c=A, M=4, act=0, rule=0, x=A, ldx=256,
+             xq=None, ldq=0, xc=None, ldc=0, bias=None, y=A, ldy=64, ws=None, wsb=0)
+    a.update(kw)
+    return mx.lib().mx_linear(a["elem"], a["layout"], a["N"], a["K"], a["w"], a["c"], a["M"],
+                              a["act"], a["rule"], a["x"], a["ldx"], a["xq"], a["ldq"], a["xc"],
+                              a["ldc"], a["bias"], a["y"], a["ldy"], a["ws"], a["wsb"], None)
+
+
+def test_linear_validation_paths():
+    assert _linear(N=40) == SHAPE
+    assert _linear(K=100) == SHAPE
+    assert _linear(M=0) == SHAPE
+    assert _linear(ldx=128) == SHAPE
+    assert _linear(ldy=32) == SHAPE
+    assert _linear(layout=1, N=48) == SHAPE
+    assert _linear(elem=1, act=1) == UNSUP
+    assert _linear(elem=1, layout=1) == UNSUP
+    assert _linear(act=2) == UNSUP
+    assert _linear(rule=3) == UNSUP
+    assert _linear(x=None) == NULL
+    assert _linear(y=None) == NULL
+    assert _linear(w=A + 8) == ALIGN
+    assert _linear(x=A + 4) == ALIGN
+    assert _linear(ldx=260) == ALIGN
+    assert _linear(ldy=68) == ALIGN
+    assert _linear(bias=A + 1) == ALIGN
+    # W8A8 quantized in the call needs a workspace
+    assert _linear(act=1) == WS
+    need = mx.mx_linear_workspace(0, 0, 64, 256, 4, 1, 0)
+    assert need >= 4 * 256 + 4 * 8
+    assert _linear(act=1, ws=A, wsb=need - 1) == WS
+    # pre-quantized activations: strides checked
+    assert _linear(act=1, x=None, xq=A, ldq=256, xc=A, ldc=4) == SHAPE
+    assert _linear(act=1, x=None, xq=A, ldq=264, xc=A, ldc=8) == ALIGN
+    # a valid call on a machine without a gfx950 device stops at the gate
+    import torch
+    if not torch.cuda.is_available():
+        assert _linear() == DEVICE
+        assert _linear(act=1, x=None, xq=A, ldq=256, xc=A, ldc=8) == DEVICE
+
+
+def test_quant_and_pack_and_moe_validation_paths():
+    L = mx.lib()
+    assert L.mx_quant_act(4, 100, A, 128, A, 128, A, 4, 0, None) == SHAPE
+    assert L.mx_quant_act(4, 128, A, 120, A, 128, A, 4, 0, None) == SHAPE
+    assert L.mx_quant_act(4, 128, A, 136, A, 136, A, 4, 0, None) == ALIGN
+    assert L.mx_quant_act(4, 128, None, 128, A, 128, A, 4, 0, None) == NULL
+    assert L.mx_quant_act(4, 128, A, 128, A, 128, A, 4, 9, None) == UNSUP
+    assert L.mx_pack_weights(0, 0, 1, 32, 128, A, A, A, A, A, 255, None) == WS
+    assert L.mx_pack_weights(0, 0, 1, 32, 128, A, A, A + 4, A, A, 256, None) == ALIGN
+    assert L.mx_pack_weights(0, 0, 1, 32, 128, A, None, A, A, A, 256, None) == NULL
+
+    def moe(**kw):
+        a = dict(elem=1, E=8, N=64, K=256, w=A, c=A, T=4, topk=2, x=A, ldx=256, ids=A,
+                 wts=None, y=A, ws=None, wsb=0)
+        a.update(kw)
+        return L.mx_moe_linear(a["elem"], a["E"], a["N"], a["K"], a["w"], a["c"], a["T"],
+                               a["topk"], a["x"], a["ldx"], a["ids"], a["wts"], a["y"], a["ws"],
+                               a["wsb"], None)
+    assert moe(topk=9) == SHAPE
+    assert moe(T=4097, topk=1) == SHAPE
+    assert moe(N=40) == SHAPE
+    assert moe(ids=None) == NULL
+    assert moe(ids=A + 2) == ALIGN
+    assert moe(wts=A) == WS
+    assert mx.mx_moe_workspace(1, 8, 64, 256, 4, 2, 1) == 4 * 2 * 64 * 4
+    import torch
+    if not torch.cuda.is_available():
+        assert moe() == DEVICE
+
+
+def test_binding_raises_without_touching_the_device():
+    with pytest.raises(mx.MXError) as ei:
+        mx.mx_packed_sizes(0, 0, 1, 24, 512)
+    assert ei.value.status == SHAPE
