@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Benchmark of the MX linear layer's hot path on one MI355X.
+
+Headline workload: the W8A8 MXFP8 decode GEMV with 32x32 block scales,
+M = 16 tokens, N = K = 7168.  One step is the whole hot path for one batch:
+per-token MXFP8 quantization of the bf16 activations (OCP rule) followed by
+the GEMV.  Weights and codes are packed once (load time, untimed); the step
+rotates over enough packed copies (>= 512 MiB) that the 256 MB Infinity
+Cache cannot serve them, so every step streams its weights from HBM.
+
+value   = algorithmic weight + scale bytes per step / step time  (GB/s)
+roofline.achieved = the same bytes / the GEMV kernel's own average duration,
+          timed with HIP events around each GEMV launch on its stream.
+
+The other workloads are timed the same way and reported under "secondary":
+M = 1 and 4 of the same GEMV, the A16W8 GEMVs (M = 1, N = 256, K = 512 and
+M = 8, N = 4096, K = 1568), the A16W4 grouped MoE GEMV (E = 32, N = K =
+3072, 16 tokens top-8) and the prefill W8A8 GEMM (M = 4096, N = K = 7168,
+quantization + GEMM per step; TFLOP/s against the 5.0 PFLOP/s fp8 peak).
+
+cpu_baseline: the CPU oracle (fp64, OpenMP) computing the headline step on
+the host cores, timed on the full workload, repeated for about 10 s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+CACHE_BYTES = 512 << 20          # rotate at least this many bytes of weights
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
+    ap.add_argument("--only", default=None,
+                    help="run one workload only (gemv16, gemv1, gemv4, a16_c1, a16_c3, moe, gemm)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Timer:
+    """K steps bracketed by synchronize; per-launch events for one kernel."""
+
+    def __init__(self, torch, steps):
+        self.torch = torch
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(steps)]
+
+    def run(self, step, kernel, steps, warmup):
+        torch = self.torch
+        for i in range(warmup):
+            step(i)
+            kernel(i, None)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(steps):
+            step(i)
+            kernel(i, self.ev[i])
+        t1.record()
+        torch.cuda.synchronize()
+        ms_step = t0.elapsed_time(t1) / steps
+        ms_kernel = sum(a.elapsed_time(b) for a, b in self.ev[:steps]) / steps
+        return ms_step, ms_kernel
+
+
+def timed_launch(ev, fn):
+    if ev is not None:
+        ev[0].record()
+    fn()
+    if ev is not None:
+        ev[1].record()
+
+
+def source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "microscaling_quantized_linear_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload, sha):
+    """HBM bytes per launch measured by rocprofv3 counters for this workload,
+    from profiles/hbm_traffic.md, if the kernel source is unchanged since."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    for m in re.finditer(r"<!--traffic (\{.*?\})-->", open(path).read()):
+        rec = json.loads(m.group(1))
+        if rec.get("workload") == workload and rec.get("source_sha") == sha:
+            return rec.get("bytes_per_launch")
+    return None
+
+
+# ---------------------------------------------------------------- workloads
+
+def setup_dense(torch, mx, g, wl, cid, M, rotate=True):
+    d = wl.linear_inputs(cid, M=M)
+    N, K = d["N"], d["K"]
+    wp, cp = g.pack(d["elem"], d["layout"], 1, N, K, d["w"], d["codes"])
+    per = wp.numel() + cp.numel()
+    copies = max(1, -(-CACHE_BYTES // per)) if rotate else 1
+    copies = min(copies, 4096)
+    wps = [wp] + [wp.clone() for _ in range(copies - 1)]
+    cps = [cp] + [cp.clone() for _ in range(copies - 1)]
+    return d, wps, cps
+
+
+def bench_w8a8_gemv(torch, mx, g, wl, M, steps, warmup):
+    d, wps, cps = setup_dense(torch, mx, g, wl, 2, M)
+    N, K = d["N"], d["K"]
+    x = g.dev(d["x"][:M])
+    xq = torch.empty((M, K), dtype=torch.uint8, device=g.DEV)
+    xc = torch.empty((M, K // 32), dtype=torch.uint8, device=g.DEV)
+    y = torch.empty((M, N), dtype=torch.int16, device=g.DEV)
+    nc = len(wps)
+
+    def step(i):
+        mx.mx_quant_act(M, K, x, K, xq, K, xc, K // 32, mx.MX_RULE_OCP)
+
+    def kernel(i, ev):
+        timed_launch(ev, lambda: mx.mx_linear(
+            mx.MX_E4M3, mx.MX_SCALE_BLK32, N, K, wps[i % nc], cps[i % nc], M, mx.MX_ACT_MXFP8,
+            mx.MX_RULE_OCP, None, 0, xq, K, xc, K // 32, None, y, N, None, 0))
+
+    ms_step, ms_k = Timer(torch, steps).run(step, kernel, steps, warmup)
+    alg = N * K + (N // 32) * (K // 32)
+    return dict(workload=f"mxfp8_w8a8_gemv_M{M}_N{N}_K{K}_blk32", M=M, N=N, K=K,
+                bytes_per_step=alg, weight_copies=nc, ms_per_step=ms_step, ms_kernel=ms_k,
+                value=alg / (ms_step * 1e-3) / 1e9, unit="GB/s",
+                kernel_gbs=alg / (ms_k * 1e-3) / 1e9, kernel="gemv_kernel (W8A8, BLK32)")
+
+
+def bench_a16_gemv(torch, mx, g, wl, cid, steps, warmup):
+    d, wps, cps = setup_dense(torch, mx, g, wl, cid, None)
+    N, K, M = d["N"], d["K"], d["M"]
+    x = g.dev(d["x"])
+    y = torch.empty((M, N), dtype=torch.int16, device=g.DEV)
+    nc = len(wps)
+
+    def kernel(i, ev):
+        timed_launch(ev, lambda: mx.mx_linear(
+            mx.MX_E4M3, mx.MX_SCALE_ROW32, N, K, wps[i % nc], cps[i % nc], M, mx.MX_ACT_BF16,
+            0, x, K, None, 0, None, 0, None, y, N, None, 0))
+
+    ms_step, ms_k = Timer(torch, steps).run(lambda i: None, kernel, steps, warmup)
+    alg = N * K + N * (K // 32)
+    return dict(workload=wl.CONFIGS[cid]["name"], M=M, N=N, K=K, bytes_per_step=alg,
+                weight_copies=nc, ms_per_step=ms_step, ms_kernel=ms_k,
+                value=alg / (ms_step * 1e-3) / 1e9, unit="GB/s",
+                kernel_gbs=alg / (ms_k * 1e-3) / 1e9, kernel="gemv_kernel (A16W8, ROW32)")
+
+
+def bench_moe(torch, mx, g, wl, steps, warmup):
+    import numpy as np
+    d = wl.moe_inputs(4)
+    E, N, K, T, topk = d["E"], d["N"], d["K"], d["T"], d["topk"]
+    wp, cp = g.pack(1, 0, E, N, K, d["w"], d["codes"])
+    per = wp.numel() + cp.numel()
+    nc = max(1, -(-CACHE_BYTES // per))
+    wps = [wp] + [wp.clone() for _ in range(nc - 1)]
+    cps = [cp] + [cp.clone() for _ in range(nc - 1)]
+    x = g.dev(d["x"])
+    ids = g.dev(d["ids"])
+    y = torch.empty((T, topk, N), dtype=torch.int16, device=g.DEV)
+
+    def kernel(i, ev):
+        timed_launch(ev, lambda: mx.mx_moe_linear(1, E, N, K, wps[i % nc], cps[i % nc], T, topk,
+                                                  x, K, ids, None, y, None, 0))
+
+    ms_step, ms_k = Timer(torch, steps).run(lambda i: None, kernel, steps, warmup)
+    touched = len(np.unique(d["ids"]))
+    alg = touched * (N * K // 2 + N * (K // 32))
+    return dict(workload=wl.CONFIGS[4]["name"], E=E, N=N, K=K, T=T, topk=topk,
+                experts_touched=touched, bytes_per_step=alg, weight_copies=nc,
+                ms_per_step=ms_step, ms_kernel=ms_k, value=alg / (ms_step * 1e-3) / 1e9,
+                unit="GB/s", kernel_gbs=alg / (ms_k * 1e-3) / 1e9,
+                kernel="gemv_kernel (A16W4, MoE)")
+
+
+def bench_gemm(torch, mx, g, wl, steps, warmup):
+    d = wl.linear_inputs(5)
+    N, K, M = d["N"], d["K"], d["M"]
+    wp, cp = g.pack(0, 1, 1, N, K, d["w"], d["codes"])
+    x = g.dev(d["x"])
+    xq = torch.empty((M, K), dtype=torch.uint8, device=g.DEV)
+    xc = torch.empty((M, K // 32), dtype=torch.uint8, device=g.DEV)
+    y = torch.empty((M, N), dtype=torch.int16, device=g.DEV)
+
+    def step(i):
+        mx.mx_quant_act(M, K, x, K, xq, K, xc, K // 32, mx.MX_RULE_OCP)
+
+    def kernel(i, ev):
+        timed_launch(ev, lambda: mx.mx_linear(
+            0, 1, N, K, wp, cp, M, mx.MX_ACT_MXFP8, 0, None, 0, xq, K, xc, K // 32, None, y, N,
+            None, 0))
+
+    ms_step, ms_k = Timer(torch, steps).run(step, kernel, steps, warmup)
+    flop = 2.0 * M * N * K
+    return dict(workload=wl.CONFIGS[5]["name"], M=M, N=N, K=K, flop_per_step=flop,
+                ms_per_step=ms_step, ms_kernel=ms_k, value=flop / (ms_step * 1e-3) / 1e12,
+                unit="TFLOP/s", kernel_tflops=flop / (ms_k * 1e-3) / 1e12,
+                kernel="gemm_w8a8_kernel (BLK32)")
+
+
+def cpu_baseline(wl):
+    import oracle
+    d = wl.linear_inputs(2, M=16)
+    N, K = d["N"], d["K"]
+    alg = N * K + (N // 32) * (K // 32)
+    runs, t_total = 0, 0.0
+    while t_total < 10.0 and runs < 20:
+        t = time.perf_counter()
+        xq, xc = oracle.quant_act(d["x"], oracle.RULE_OCP)
+        oracle.linear(0, 1, N, K, d["w"], d["codes"], 16, oracle.ACT_MXFP8, xq=xq, xcodes=xc)
+        t_total += time.perf_counter() - t
+        runs += 1
+    sec = t_total / runs
+    return {"value": alg / sec / 1e9, "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"the full headline step (M=16, N=K=7168: quant + fp64 linear), "
+                      f"{runs} runs, {sec:.2f} s each"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is "
+              "a single-GPU kernel library and this build measures no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import microscaling_quantized_linear_amd as mx
+    from microscaling_quantized_linear_amd import workloads as wl
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import mxgpu as g
+
+    mx.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a gfx950 GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    K, W = args.steps, args.warmup
+
+    only = args.only
+    want = (lambda n: only is None or only == n)
+    head = None
+    sec = []
+    if want("gemv16"):
+        log("headline: W8A8 GEMV M=16 N=K=7168")
+        head = bench_w8a8_gemv(torch, mx, g, wl, 16, K, W)
+        log(json.dumps(head))
+    if not args.no_secondary:
+        if want("gemv1"):
+            sec.append(bench_w8a8_gemv(torch, mx, g, wl, 1, K, W)); log(json.dumps(sec[-1]))
+        if want("gemv4"):
+            sec.append(bench_w8a8_gemv(torch, mx, g, wl, 4, K, W)); log(json.dumps(sec[-1]))
+        if want("a16_c1"):
+            sec.append(bench_a16_gemv(torch, mx, g, wl, 1, K, W)); log(json.dumps(sec[-1]))
+        if want("a16_c3"):
+            sec.append(bench_a16_gemv(torch, mx, g, wl, 3, K, W)); log(json.dumps(sec[-1]))
+        if want("moe"):
+            sec.append(bench_moe(torch, mx, g, wl, K, W)); log(json.dumps(sec[-1]))
+        if want("gemm"):
+            sec.append(bench_gemm(torch, mx, g, wl, max(10, K // 4), max(3, W // 4)))
+            log(json.dumps(sec[-1]))
+    if head is None:
+        head = sec[0]
+    for s in sec:
+        if s["unit"] == "GB/s":
+            s["roofline_frac"] = round(s["kernel_gbs"] / HBM_PEAK_GBS, 4)
+        else:
+            s["roofline_frac"] = round(s["kernel_tflops"] / FP8_PEAK_TFLOPS, 4)
+
+    sha = source_sha("mx_gemv.hip", "mx_device.h")
+    if head["unit"] == "GB/s":
+        roof = {"bound": "hbm", "achieved": round(head["kernel_gbs"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(head["kernel_gbs"] / HBM_PEAK_GBS, 4),
+                "traffic": recorded_traffic(head["workload"], sha)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(head["kernel_tflops"], 1),
+                "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(head["kernel_tflops"] / FP8_PEAK_TFLOPS, 4), "traffic": None}
+    cpu = None if args.no_cpu else cpu_baseline(wl)
+    out = {
+        "metric": "achieved HBM GB/s (weights+scales) for M≤16 MX GEMV; TFLOP/s for M=4096 GEMM",
+        "value": round(head["value"], 1),
+        "unit": head["unit"],
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8",
+        "data": "synthetic",
+        "config": {"workload": head["workload"], "M": head.get("M"), "N": head.get("N"),
+                   "K": head.get("K"), "step": "per-token MXFP8 quant (OCP rule) + GEMV",
+                   "weight_copies_rotated": head.get("weight_copies"),
+                   "gemv_kernel_ms": round(head["ms_kernel"], 5)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "secondary": [{k: (round(v, 5) if isinstance(v, float) else v) for k, v in s.items()}
+                      for s in sec],
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -74,6 +74,8 @@ def _declare(L):
     L.orc_moe_linear.argtypes = [i32, i64, i64, i64, p, p, i64, i64, p, i64, p,
                                  p, p]
     L.orc_moe_linear.restype = None
+    L.orc_threads.argtypes = []
+    L.orc_threads.restype = i32
 
 
 def _ptr(a):
@@ -200,3 +202,8 @@ def moe_linear(elem, E, N, K, w, codes, x, ids, weights=None):
     lib().orc_moe_linear(elem, E, N, K, _ptr(w), _ptr(codes), T, topk, _ptr(x),
                          x.shape[1], _ptr(ids), _ptr(weights), _ptr(y))
     return y
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's loops run on."""
+    return lib().orc_threads()

@@ -38,6 +38,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 enum { ORC_E4M3 = 0, ORC_E2M1 = 1 };
 enum { ORC_ROW32 = 0, ORC_BLK32 = 1 };
@@ -445,4 +448,14 @@ void orc_moe_linear(int elem, int64_t E, int64_t N, int64_t K, const uint8_t *w,
                     y[(t * topk + k) * N + n] = s;
             }
     }
+}
+
+/* Threads the OpenMP loops above use (1 without OpenMP). */
+int orc_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

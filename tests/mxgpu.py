@@ -96,17 +96,30 @@ def rounding_floor(ref: np.ndarray) -> float:
     return float(np.linalg.norm(r - ref) / n) if n > 0 else 0.0
 
 
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |v| (8 significant bits)."""
+    a = np.maximum(np.abs(v), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
 def assert_close(y_bits: np.ndarray, ref: np.ndarray, what: str = ""):
     """The bar: relative L2 <= 2e-3 and every |err| <= 1e-2 * max|oracle row|.
-    On cases with few outputs the bf16 rounding of the exact result alone can
-    exceed 2e-3; there the relative-L2 bar is 2% above that floor instead."""
+
+    Where the exact result rounded once to bf16 does not itself reach the
+    2e-3 bar (cases with few outputs: the rounding floor of the relative L2
+    is then >= 1.9e-3), the relative-L2 test is replaced by a per-element one:
+    every output within one bf16 ulp of the exact result, i.e. the correctly
+    rounded value or its neighbour."""
     y = bf16_to_f64(y_bits).reshape(ref.shape)
     assert np.all(np.isfinite(y)), f"{what}: non-finite output"
     err = y - ref
     nref = np.linalg.norm(ref)
     rel = np.linalg.norm(err) / nref if nref > 0 else np.linalg.norm(err)
-    bar = max(REL_L2, 1.02 * rounding_floor(ref))
-    assert rel <= bar, f"{what}: relative L2 {rel:.3e} > {bar:.3e}"
+    if rel > REL_L2:
+        floor = rounding_floor(ref)
+        assert floor >= 0.95 * REL_L2, f"{what}: relative L2 {rel:.3e} > {REL_L2} (floor {floor:.3e})"
+        far = np.abs(err) > bf16_ulp(ref)
+        assert not far.any(), f"{what}: {far.sum()} outputs more than one bf16 ulp off"
     r2 = ref.reshape(-1, ref.shape[-1])
     e2 = np.abs(err.reshape(-1, ref.shape[-1]))
     rowmax = np.abs(r2).max(axis=1, keepdims=True)
