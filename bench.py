@@ -9,8 +9,10 @@ rotates over enough packed copies (>= 512 MiB) that the 256 MB Infinity
 Cache cannot serve them, so every step streams its weights from HBM.
 
 value   = algorithmic weight + scale bytes per step / step time  (GB/s)
-roofline.achieved = the same bytes / the GEMV kernel's own average duration,
-          timed with HIP events around each GEMV launch on its stream.
+roofline.achieved = the same bytes / the GEMV kernel's average duration per
+          launch: `steps` GEMV launches replayed back to back from a HIP graph
+          on the library's stream, timed with HIP events (inter-launch gaps
+          included, so this is a lower bound on the kernel's own rate).
 
 The other workloads are timed the same way and reported under "secondary":
 M = 1 and 4 of the same GEMV, the A16W8 GEMVs (M = 1, N = 256, K = 512 and
@@ -55,39 +57,50 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-class Timer:
-    """K steps bracketed by synchronize; per-launch events for one kernel."""
+class GraphTimer:
+    """Times steps captured in a HIP graph.
 
-    def __init__(self, torch, steps):
+    Submitting one step from Python takes longer than the GPU needs to run
+    it, so the steps are captured once (torch.cuda.CUDAGraph over the stream
+    the library launches on) and the timed region is one replay of a graph
+    holding exactly `steps` steps, bracketed by synchronize and HIP events.
+    This is how a serving loop runs them (and how the pages tune their decode
+    tiles: by graph replay latency)."""
+
+    def __init__(self, torch):
         self.torch = torch
-        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(steps)]
 
-    def run(self, step, kernel, steps, warmup):
+    def _graph(self, fn, n):
         torch = self.torch
-        for i in range(warmup):
-            step(i)
-            kernel(i, None)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, capture_error_mode="thread_local"):
+            for i in range(n):
+                fn(i)
+        return g
+
+    def time(self, fn, steps, warmup):
+        """ms per call of fn(i), over `steps` calls replayed back to back."""
+        torch = self.torch
+        for i in range(2):
+            fn(i)                      # eager first calls (one-time setup)
+        torch.cuda.synchronize()
+        gw = self._graph(fn, max(warmup, 1))
+        gt = self._graph(fn, steps)
+        gw.replay()
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record()
-        for i in range(steps):
-            step(i)
-            kernel(i, self.ev[i])
+        gt.replay()
         t1.record()
         torch.cuda.synchronize()
-        ms_step = t0.elapsed_time(t1) / steps
-        ms_kernel = sum(a.elapsed_time(b) for a, b in self.ev[:steps]) / steps
+        return t0.elapsed_time(t1) / steps
+
+    def run(self, step, kernel, steps, warmup):
+        """(ms per step, ms per launch of the dominant kernel alone)."""
+        ms_step = self.time(lambda i: (step(i), kernel(i)), steps, warmup)
+        ms_kernel = self.time(kernel, steps, warmup)
         return ms_step, ms_kernel
-
-
-def timed_launch(ev, fn):
-    if ev is not None:
-        ev[0].record()
-    fn()
-    if ev is not None:
-        ev[1].record()
 
 
 def source_sha(*names):
@@ -137,12 +150,12 @@ def bench_w8a8_gemv(torch, mx, g, wl, M, steps, warmup):
     def step(i):
         mx.mx_quant_act(M, K, x, K, xq, K, xc, K // 32, mx.MX_RULE_OCP)
 
-    def kernel(i, ev):
-        timed_launch(ev, lambda: mx.mx_linear(
-            mx.MX_E4M3, mx.MX_SCALE_BLK32, N, K, wps[i % nc], cps[i % nc], M, mx.MX_ACT_MXFP8,
-            mx.MX_RULE_OCP, None, 0, xq, K, xc, K // 32, None, y, N, None, 0))
+    def kernel(i):
+        mx.mx_linear(mx.MX_E4M3, mx.MX_SCALE_BLK32, N, K, wps[i % nc], cps[i % nc], M,
+                     mx.MX_ACT_MXFP8, mx.MX_RULE_OCP, None, 0, xq, K, xc, K // 32, None, y, N,
+                     None, 0)
 
-    ms_step, ms_k = Timer(torch, steps).run(step, kernel, steps, warmup)
+    ms_step, ms_k = GraphTimer(torch).run(step, kernel, steps, warmup)
     alg = N * K + (N // 32) * (K // 32)
     return dict(workload=f"mxfp8_w8a8_gemv_M{M}_N{N}_K{K}_blk32", M=M, N=N, K=K,
                 bytes_per_step=alg, weight_copies=nc, ms_per_step=ms_step, ms_kernel=ms_k,
@@ -157,12 +170,12 @@ def bench_a16_gemv(torch, mx, g, wl, cid, steps, warmup):
     y = torch.empty((M, N), dtype=torch.int16, device=g.DEV)
     nc = len(wps)
 
-    def kernel(i, ev):
-        timed_launch(ev, lambda: mx.mx_linear(
-            mx.MX_E4M3, mx.MX_SCALE_ROW32, N, K, wps[i % nc], cps[i % nc], M, mx.MX_ACT_BF16,
-            0, x, K, None, 0, None, 0, None, y, N, None, 0))
+    def kernel(i):
+        mx.mx_linear(mx.MX_E4M3, mx.MX_SCALE_ROW32, N, K, wps[i % nc], cps[i % nc], M,
+                     mx.MX_ACT_BF16, 0, x, K, None, 0, None, 0, None, y, N, None, 0)
 
-    ms_step, ms_k = Timer(torch, steps).run(lambda i: None, kernel, steps, warmup)
+    ms_k = GraphTimer(torch).time(kernel, steps, warmup)
+    ms_step = ms_k
     alg = N * K + N * (K // 32)
     return dict(workload=wl.CONFIGS[cid]["name"], M=M, N=N, K=K, bytes_per_step=alg,
                 weight_copies=nc, ms_per_step=ms_step, ms_kernel=ms_k,
@@ -183,11 +196,12 @@ def bench_moe(torch, mx, g, wl, steps, warmup):
     ids = g.dev(d["ids"])
     y = torch.empty((T, topk, N), dtype=torch.int16, device=g.DEV)
 
-    def kernel(i, ev):
-        timed_launch(ev, lambda: mx.mx_moe_linear(1, E, N, K, wps[i % nc], cps[i % nc], T, topk,
-                                                  x, K, ids, None, y, None, 0))
+    def kernel(i):
+        mx.mx_moe_linear(1, E, N, K, wps[i % nc], cps[i % nc], T, topk, x, K, ids, None, y, None,
+                         0)
 
-    ms_step, ms_k = Timer(torch, steps).run(lambda i: None, kernel, steps, warmup)
+    ms_k = GraphTimer(torch).time(kernel, steps, warmup)
+    ms_step = ms_k
     touched = len(np.unique(d["ids"]))
     alg = touched * (N * K // 2 + N * (K // 32))
     return dict(workload=wl.CONFIGS[4]["name"], E=E, N=N, K=K, T=T, topk=topk,
@@ -209,12 +223,11 @@ def bench_gemm(torch, mx, g, wl, steps, warmup):
     def step(i):
         mx.mx_quant_act(M, K, x, K, xq, K, xc, K // 32, mx.MX_RULE_OCP)
 
-    def kernel(i, ev):
-        timed_launch(ev, lambda: mx.mx_linear(
-            0, 1, N, K, wp, cp, M, mx.MX_ACT_MXFP8, 0, None, 0, xq, K, xc, K // 32, None, y, N,
-            None, 0))
+    def kernel(i):
+        mx.mx_linear(0, 1, N, K, wp, cp, M, mx.MX_ACT_MXFP8, 0, None, 0, xq, K, xc, K // 32,
+                     None, y, N, None, 0)
 
-    ms_step, ms_k = Timer(torch, steps).run(step, kernel, steps, warmup)
+    ms_step, ms_k = GraphTimer(torch).run(step, kernel, steps, warmup)
     flop = 2.0 * M * N * K
     return dict(workload=wl.CONFIGS[5]["name"], M=M, N=N, K=K, flop_per_step=flop,
                 ms_per_step=ms_step, ms_kernel=ms_k, value=flop / (ms_step * 1e-3) / 1e12,

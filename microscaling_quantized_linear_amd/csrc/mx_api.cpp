@@ -58,17 +58,31 @@ mx_status device_ok() {
 
 mx_status launched(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH; }
 
-// waves per GEMV workgroup; MX_GEMV_WAVES (1, 2, 4, 8) overrides, read once
-int gemv_waves(int64_t S) {
-    static const int forced = [] {
-        const char *s = std::getenv("MX_GEMV_WAVES");
-        const int v = s ? std::atoi(s) : 0;
-        return (v == 1 || v == 2 || v == 4 || v == 8) ? v : 0;
-    }();
-    if (forced) return forced;
-    if (S >= 32) return 8;
-    if (S >= 8) return 4;
-    return S >= 2 ? 2 : 1;
+int env_choice(const char *name) {
+    const char *s = std::getenv(name);
+    const int v = s ? std::atoi(s) : 0;
+    return (v == 1 || v == 2 || v == 4 || v == 8) ? v : 0;
+}
+
+// Launch shape of the GEMV (see mx_kernels.h).  MX_GEMV_WAVES, MX_GEMV_CHUNK
+// and MX_GEMV_TILES override it (tuning sweeps only; read once).
+// Defaults measured on MI355X with graph-replayed launches: long K (S >= 32
+// steps, e.g. 7168) 8 waves x chunks of 4 steps x 2 tiles; shorter K 4 waves
+// x 4 steps x 1 tile; grouped MoE 4 waves x 2 steps x 4 tiles of an expert.
+mx::GemvShape gemv_shape(int64_t S, bool moe) {
+    static const int f_nw = env_choice("MX_GEMV_WAVES"), f_chunk = env_choice("MX_GEMV_CHUNK"),
+                     f_tiles = env_choice("MX_GEMV_TILES");
+    mx::GemvShape g;
+    if (moe)
+        g = {S >= 8 ? 4 : S >= 2 ? 2 : 1, 2, 4};
+    else if (S >= 32)
+        g = {8, 4, 2};
+    else
+        g = {S >= 8 ? 4 : S >= 2 ? 2 : 1, 4, 1};
+    if (f_nw) g.nw = f_nw;
+    if (f_chunk) g.chunk = f_chunk < 2 ? 2 : f_chunk;
+    if (f_tiles) g.tiles = f_tiles > 4 ? 4 : f_tiles;
+    return g;
 }
 
 // largest M served by the decode GEMV for W8A8; above it the GEMM runs
@@ -249,7 +263,7 @@ mx_status mx_linear(int elem, int layout, int64_t N, int64_t K, const void *w_pa
     a.bias = static_cast<const uint16_t *>(bias);
     a.y = static_cast<uint16_t *>(y);
     a.ldy = ldy;
-    return launched(mx::launch_gemv(elem, layout, act, false, a, gemv_waves(Kp / 128), s));
+    return launched(mx::launch_gemv(elem, layout, act, false, a, gemv_shape(Kp / 128, false), s));
 }
 
 mx_status mx_moe_workspace(int elem, int64_t E, int64_t N, int64_t K, int64_t T, int64_t topk,
@@ -296,8 +310,8 @@ mx_status mx_moe_linear(int elem, int64_t E, int64_t N, int64_t K, const void *w
     a.y = static_cast<uint16_t *>(y);
     a.ldy = N;
     a.ws = topk_weights ? static_cast<float *>(ws) : nullptr;
-    const int nw = gemv_waves(Kp / 128) > 4 ? 4 : gemv_waves(Kp / 128);
-    if ((st = launched(mx::launch_gemv(elem, ROW32, ACT_BF16, true, a, nw, s))) != MX_OK)
+    if ((st = launched(mx::launch_gemv(elem, ROW32, ACT_BF16, true, a,
+                                       gemv_shape(Kp / 128, true), s))) != MX_OK)
         return st;
     if (topk_weights)
         return launched(mx::launch_moe_combine(T, topk, N, static_cast<const float *>(ws),

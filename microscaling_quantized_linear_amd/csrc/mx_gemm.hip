@@ -185,9 +185,18 @@ static hipError_t launch_ntw(const GemmArgs &a, hipStream_t st) {
     constexpr int BN = 2 * NTW * 16;
     const int64_t tiles = ((a.N + BN - 1) / BN) * ((a.M + kBM - 1) / kBM);
     const int smem = GemmSmem<NTW>::kTotal;
-    hipError_t e = hipFuncSetAttribute((const void *)gemm_w8a8_kernel<LAYOUT, NTW>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    // the LDS-size attribute is set once per device (outside any graph capture
+    // that follows the first call)
+    static bool attr_done[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64 || !attr_done[dev]) {
+        e = hipFuncSetAttribute((const void *)gemm_w8a8_kernel<LAYOUT, NTW>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+        if (e != hipSuccess) return e;
+        if (dev >= 0 && dev < 64) attr_done[dev] = true;
+    }
     hipLaunchKernelGGL((gemm_w8a8_kernel<LAYOUT, NTW>), dim3((unsigned)tiles), dim3(256), smem, st,
                        a);
     return hipGetLastError();

@@ -28,40 +28,47 @@
 
 namespace mx {
 
+template <int G>
 struct StepW8A8 {
-    v4u a0, a1, b0, b1;
-    uint32_t cw, cx;
+    v4u a0[G], a1[G], b0, b1;
+    uint32_t cw[G], cx;
 };
+template <int G>
 struct StepA16 {
-    v4u a0, a1;           // e4m3: two halves; e2m1: a0 only
+    v4u a0[G], a1[G];     // e4m3: two halves; e2m1: a0 only
     v4u x0, x1, x2, x3;   // bf16 activations of the four MFMAs
-    uint32_t cw;
+    uint32_t cw[G];
 };
 
-template <int ELEM, int LAYOUT, int ACT, bool MOE, int NW>
+// G: weight tiles per workgroup.  A wavefront's activation fragment of a step
+// is loaded once and feeds the G tiles' matrix-core operations.
+template <int ELEM, int LAYOUT, int ACT, bool MOE, int NW, int P, int G>
 __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
     const int r = lane % 16, j = lane / 16;
     const int64_t Kp = (p.K + 127) / 128 * 128, S = Kp / 128, T = p.N / 16, Q = (S + 3) / 4;
     const int64_t KB = p.K / 32;
-    const int64_t unit = blockIdx.x;                 // e * T + t
-    const int64_t e = MOE ? unit / T : 0, t = MOE ? unit % T : unit;
+    const int64_t TG = (T + G - 1) / G;              // tile groups per expert
+    const int64_t unit = blockIdx.x;                 // e * TG + tg
+    const int64_t e = MOE ? unit / TG : 0, tg = MOE ? unit % TG : unit;
+    const int64_t t0 = tg * G;
+    const int ntiles = (int)(T - t0 < G ? T - t0 : G);
     constexpr int CHUNK = ELEM == E4M3 ? 2048 : 1024;
 
     __shared__ uint16_t slots[MOE ? kMoeMaxPairs : 1];
     __shared__ int nslots_sh;
-    __shared__ v4f red[NW > 1 ? NW : 1][64];
+    __shared__ v4f red[NW > 1 ? NW : 1][G][64];
 
     int64_t nslots;
     if (MOE) {
-        const int64_t P = p.rows * p.topk;
+        const int64_t npairs = p.rows * p.topk;
         if (wave == 0) {
             int running = 0;
-            for (int64_t base = 0; base < P; base += 64) {
+            for (int64_t base = 0; base < npairs; base += 64) {
                 const int64_t i = base + lane;
                 // unit e == E collects the pairs whose id is out of range
-                const int32_t id = i < P ? p.ids[i] : 0;
-                const bool hit = i < P && (e < p.E ? id == (int32_t)e : (id < 0 || id >= p.E));
+                const int32_t id = i < npairs ? p.ids[i] : 0;
+                const bool hit = i < npairs && (e < p.E ? id == (int32_t)e : (id < 0 || id >= p.E));
                 const uint64_t mask = __ballot(hit);
                 const int rank = running + __popcll(mask & ((1ull << lane) - 1ull));
                 if (hit) slots[rank] = (uint16_t)i;
@@ -73,8 +80,9 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
         nslots = nslots_sh;
         if (nslots == 0) return;                     // no token: no weight bytes read
         if (e == p.E) {                              // out-of-range ids: zero rows
-            for (int64_t idx = threadIdx.x; idx < nslots * 16; idx += NW * 64) {
-                const int64_t pair = slots[idx / 16], n = 16 * t + idx % 16;
+            for (int64_t idx = threadIdx.x; idx < nslots * 16 * ntiles; idx += NW * 64) {
+                const int64_t pair = slots[idx / (16 * ntiles)];
+                const int64_t n = 16 * t0 + idx % (16 * ntiles);
                 if (p.ws)
                     p.ws[pair * p.N + n] = 0.f;
                 else
@@ -86,14 +94,17 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
         nslots = p.rows;
     }
 
-    // resources: the tile's weight chunks, its codes, the activations
+    // resources: the group's weight chunks, codes, the activations
     const __amdgpu_buffer_rsrc_t wr =
-        make_rsrc(p.w + unit * S * CHUNK, (uint32_t)(S * CHUNK));
+        make_rsrc(p.w + (e * T + t0) * S * CHUNK, (uint32_t)(ntiles * S * CHUNK));
     __amdgpu_buffer_rsrc_t cr;
     if (LAYOUT == ROW32)
-        cr = make_rsrc(p.codes + unit * Q * 256, (uint32_t)(Q * 256));
+        cr = make_rsrc(p.codes + (e * T + t0) * Q * 256, (uint32_t)(ntiles * Q * 256));
     else
-        cr = make_rsrc(p.codes + ((e * p.N + 16 * t) / 32) * (Kp / 32), (uint32_t)(Kp / 32));
+        cr = make_rsrc(p.codes, (uint32_t)(p.E * (p.N / 32) * (Kp / 32)));
+    uint32_t crow[G];                                // BLK32: code row offset of each tile
+#pragma unroll
+    for (int g = 0; g < G; ++g) crow[g] = (uint32_t)(((e * p.N + 16 * (t0 + g)) / 32) * (Kp / 32));
     const int64_t xelt = ACT == ACT_MXFP8 ? 1 : 2;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, (uint32_t)(p.xrows * p.ldx * xelt));
     const __amdgpu_buffer_rsrc_t xcr =
@@ -102,6 +113,16 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
     const int64_t s0 = (wave * S) / NW, s1 = ((wave + 1) * S) / NW;
     const int64_t batches = (nslots + 15) / 16;
     const int64_t b_first = MOE ? 0 : blockIdx.y, b_last = MOE ? batches : blockIdx.y + 1;
+
+    // weight and code offsets of tile g at step s (out of range beyond s1)
+    auto woff = [&](int g, int64_t s, bool in) -> uint32_t {
+        return in ? (uint32_t)((g * S + s) * CHUNK + 16 * lane) : kOOB;
+    };
+    auto coff = [&](int g, int64_t s, bool in) -> uint32_t {
+        if (!in) return kOOB;
+        if (LAYOUT == ROW32) return (uint32_t)((g * Q + s / 4) * 256 + 4 * lane);
+        return crow[g] + (uint32_t)(4 * s);
+    };
 
     for (int64_t bi = b_first; bi < b_last; ++bi) {
         // this lane's slot: activation row and output row (or -1)
@@ -121,133 +142,161 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
         const uint32_t xbase = live ? (uint32_t)(xrow * p.ldx * xelt) : 0u;
         const uint32_t cxbase = live ? (uint32_t)(xrow * p.ldc) : 0u;
 
-        v4f acc = {0.f, 0.f, 0.f, 0.f};
+        v4f acc[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
 
         if (ACT == ACT_MXFP8) {
             // ---- W8A8: e4m3 weights x MXFP8 activations, scaled MFMA ----
+            // a step outside [s0, s1) reads only zeros (out-of-range offsets)
             auto load = [&](int64_t s) {
-                StepW8A8 st;
-                st.a0 = load16<kNT>(wr, (uint32_t)(s * 2048 + 16 * lane));
-                st.a1 = load16<kNT>(wr, (uint32_t)(s * 2048 + 1024 + 16 * lane));
+                StepW8A8<G> st;
+                const bool in = s < s1;
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const uint32_t wo = woff(g, s, in);
+                    st.a0[g] = load16<kNT>(wr, wo);
+                    st.a1[g] = load16<kNT>(wr, in ? wo + 1024u : kOOB);
+                }
                 const int64_t k0 = 128 * s + 16 * j, k1 = k0 + 64;   // K of each 16-byte half
-                st.b0 = load16(xr, live && k0 < p.K ? xbase + (uint32_t)k0 : kOOB);
-                st.b1 = load16(xr, live && k1 < p.K ? xbase + (uint32_t)k1 : kOOB);
+                st.b0 = load16(xr, in && live && k0 < p.K ? xbase + (uint32_t)k0 : kOOB);
+                st.b1 = load16(xr, in && live && k1 < p.K ? xbase + (uint32_t)k1 : kOOB);
                 const int64_t blk = 4 * s + j;                       // scale block of lane group j
-                st.cx = load1(xcr, live && blk < KB ? cxbase + (uint32_t)blk : kOOB);
-                if (LAYOUT == ROW32)
-                    st.cw = load4(cr, (uint32_t)((s / 4) * 256 + 4 * lane));
-                else
-                    st.cw = load4(cr, (uint32_t)(4 * s));
+                st.cx = load1(xcr, in && live && blk < KB ? cxbase + (uint32_t)blk : kOOB);
+#pragma unroll
+                for (int g = 0; g < G; ++g) st.cw[g] = load4(cr, coff(g, s, in));
                 return st;
             };
-            auto compute = [&](const StepW8A8 &st, int64_t s, v4f c) {
-                const uint32_t sw = LAYOUT == ROW32 ? byte_of(st.cw, (uint32_t)(s % 4))
-                                                    : byte_of(st.cw, (uint32_t)j);
-                return mfma_fp8_scaled(cat8(st.a0, st.a1), cat8(st.b0, st.b1), c, (int)sw,
-                                       (int)st.cx);
+            auto compute = [&](const StepW8A8<G> &st, int64_t s) {
+                const v8i b = cat8(st.b0, st.b1);
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const uint32_t sw = LAYOUT == ROW32 ? byte_of(st.cw[g], (uint32_t)(s % 4))
+                                                        : byte_of(st.cw[g], (uint32_t)j);
+                    acc[g] = mfma_fp8_scaled(cat8(st.a0[g], st.a1[g]), b, acc[g], (int)sw,
+                                             (int)st.cx);
+                }
             };
-            int64_t s = s0;
-            for (; s + 4 <= s1; s += 4) {
-                StepW8A8 st[4];
+            // all loads of a chunk of P steps are issued before its first MFMA
+            for (int64_t c = s0; c < s1; c += P) {
+                StepW8A8<G> st[P];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) st[u] = load(s + u);
+                for (int u = 0; u < P; ++u) st[u] = load(c + u);
+                // keep the scheduler from pulling MFMAs (and their waits) up
+                // between the loads: all P steps stay in flight together
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) acc = compute(st[u], s + u, acc);
+                for (int u = 0; u < P; ++u) compute(st[u], c + u);
             }
-            for (; s < s1; ++s) acc = compute(load(s), s, acc);
         } else {
             // ---- A16: bf16 activations, weights decoded in registers ----
             auto load = [&](int64_t s) {
-                StepA16 st;
+                StepA16<G> st;
+                const bool in = s < s1;
                 if (ELEM == E4M3) {
-                    st.a0 = load16<kNT>(wr, (uint32_t)(s * 2048 + 16 * lane));
-                    st.a1 = load16<kNT>(wr, (uint32_t)(s * 2048 + 1024 + 16 * lane));
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const uint32_t wo = woff(g, s, in);
+                        st.a0[g] = load16<kNT>(wr, wo);
+                        st.a1[g] = load16<kNT>(wr, in ? wo + 1024u : kOOB);
+                    }
                     // MFMA d covers K 16 j + 8 d (d < 2) and 64 + 16 j + 8 (d - 2)
                     const int64_t k0 = 128 * s + 16 * j, k1 = k0 + 64;
-                    const bool v0 = live && k0 < p.K, v1 = live && k1 < p.K;
+                    const bool v0 = in && live && k0 < p.K, v1 = in && live && k1 < p.K;
                     st.x0 = load16(xr, v0 ? xbase + (uint32_t)(2 * k0) : kOOB);
                     st.x1 = load16(xr, v0 ? xbase + (uint32_t)(2 * k0 + 16) : kOOB);
                     st.x2 = load16(xr, v1 ? xbase + (uint32_t)(2 * k1) : kOOB);
                     st.x3 = load16(xr, v1 ? xbase + (uint32_t)(2 * k1 + 16) : kOOB);
                 } else {
-                    st.a0 = load16<kNT>(wr, (uint32_t)(s * 1024 + 16 * lane));
+#pragma unroll
+                    for (int g = 0; g < G; ++g) st.a0[g] = load16<kNT>(wr, woff(g, s, in));
                     const int64_t k0 = 128 * s + 32 * j;            // the lane's whole block
-                    const bool v0 = live && k0 < p.K;
+                    const bool v0 = in && live && k0 < p.K;
                     st.x0 = load16(xr, v0 ? xbase + (uint32_t)(2 * k0) : kOOB);
                     st.x1 = load16(xr, v0 ? xbase + (uint32_t)(2 * k0 + 16) : kOOB);
                     st.x2 = load16(xr, v0 ? xbase + (uint32_t)(2 * k0 + 32) : kOOB);
                     st.x3 = load16(xr, v0 ? xbase + (uint32_t)(2 * k0 + 48) : kOOB);
                 }
-                if (LAYOUT == ROW32)
-                    st.cw = load4(cr, (uint32_t)((s / 4) * 256 + 4 * lane));
-                else
-                    st.cw = load4(cr, (uint32_t)(4 * s));
+#pragma unroll
+                for (int g = 0; g < G; ++g) st.cw[g] = load4(cr, coff(g, s, in));
                 return st;
             };
-            auto compute = [&](const StepA16 &st, int64_t s, v4f c) {
-                if (ELEM == E4M3) {
-                    // codes of the blocks holding K 16 j.. (block j/2) and 64 + 16 j..
-                    // (block 2 + j/2) of this lane's row
-                    uint32_t c0, c1;
-                    if (LAYOUT == ROW32) {
-                        const uint32_t u = (uint32_t)(s % 4);
-                        c0 = byte_of((uint32_t)__shfl((int)st.cw, 16 * (j / 2) + r), u);
-                        c1 = byte_of((uint32_t)__shfl((int)st.cw, 16 * (2 + j / 2) + r), u);
+            auto compute = [&](const StepA16<G> &st, int64_t s) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    if (ELEM == E4M3) {
+                        // codes of the blocks holding K 16 j.. (block j/2) and
+                        // 64 + 16 j.. (block 2 + j/2) of this lane's row
+                        uint32_t c0, c1;
+                        if (LAYOUT == ROW32) {
+                            const uint32_t u = (uint32_t)(s % 4);
+                            c0 = byte_of((uint32_t)__shfl((int)st.cw[g], 16 * (j / 2) + r), u);
+                            c1 = byte_of((uint32_t)__shfl((int)st.cw[g], 16 * (2 + j / 2) + r), u);
+                        } else {
+                            c0 = byte_of(st.cw[g], (uint32_t)(j / 2));
+                            c1 = byte_of(st.cw[g], (uint32_t)(2 + j / 2));
+                        }
+                        const float f0 = code_as_scale(c0), f1 = code_as_scale(c1);
+                        v4f c = acc[g];
+                        c = mfma_bf16(dec8_e4m3(st.a0[g][0], st.a0[g][1], f0), as_bf16x8(st.x0), c);
+                        c = mfma_bf16(dec8_e4m3(st.a0[g][2], st.a0[g][3], f0), as_bf16x8(st.x1), c);
+                        c = mfma_bf16(dec8_e4m3(st.a1[g][0], st.a1[g][1], f1), as_bf16x8(st.x2), c);
+                        c = mfma_bf16(dec8_e4m3(st.a1[g][2], st.a1[g][3], f1), as_bf16x8(st.x3), c);
+                        acc[g] = c;
                     } else {
-                        c0 = byte_of(st.cw, (uint32_t)(j / 2));
-                        c1 = byte_of(st.cw, (uint32_t)(2 + j / 2));
+                        const uint32_t cc = LAYOUT == ROW32 ? byte_of(st.cw[g], (uint32_t)(s % 4))
+                                                            : byte_of(st.cw[g], (uint32_t)j);
+                        const float f = code_as_scale(cc);
+                        v4f c = acc[g];
+                        c = mfma_bf16(dec8_e2m1(st.a0[g][0], f), as_bf16x8(st.x0), c);
+                        c = mfma_bf16(dec8_e2m1(st.a0[g][1], f), as_bf16x8(st.x1), c);
+                        c = mfma_bf16(dec8_e2m1(st.a0[g][2], f), as_bf16x8(st.x2), c);
+                        c = mfma_bf16(dec8_e2m1(st.a0[g][3], f), as_bf16x8(st.x3), c);
+                        acc[g] = c;
                     }
-                    const float f0 = code_as_scale(c0), f1 = code_as_scale(c1);
-                    c = mfma_bf16(dec8_e4m3(st.a0[0], st.a0[1], f0), as_bf16x8(st.x0), c);
-                    c = mfma_bf16(dec8_e4m3(st.a0[2], st.a0[3], f0), as_bf16x8(st.x1), c);
-                    c = mfma_bf16(dec8_e4m3(st.a1[0], st.a1[1], f1), as_bf16x8(st.x2), c);
-                    c = mfma_bf16(dec8_e4m3(st.a1[2], st.a1[3], f1), as_bf16x8(st.x3), c);
-                } else {
-                    const uint32_t cc = LAYOUT == ROW32 ? byte_of(st.cw, (uint32_t)(s % 4))
-                                                        : byte_of(st.cw, (uint32_t)j);
-                    const float f = code_as_scale(cc);
-                    c = mfma_bf16(dec8_e2m1(st.a0[0], f), as_bf16x8(st.x0), c);
-                    c = mfma_bf16(dec8_e2m1(st.a0[1], f), as_bf16x8(st.x1), c);
-                    c = mfma_bf16(dec8_e2m1(st.a0[2], f), as_bf16x8(st.x2), c);
-                    c = mfma_bf16(dec8_e2m1(st.a0[3], f), as_bf16x8(st.x3), c);
                 }
-                return c;
             };
-            int64_t s = s0;
-            for (; s + 4 <= s1; s += 4) {
-                StepA16 st[4];
+            for (int64_t c = s0; c < s1; c += P) {
+                StepA16<G> st[P];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) st[u] = load(s + u);
+                for (int u = 0; u < P; ++u) st[u] = load(c + u);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) acc = compute(st[u], s + u, acc);
+                for (int u = 0; u < P; ++u) compute(st[u], c + u);
             }
-            for (; s < s1; ++s) acc = compute(load(s), s, acc);
         }
 
         // ---- reduce the NW partial tiles in wave order, then store ----
         if (NW > 1) {
-            red[wave][lane] = acc;
+#pragma unroll
+            for (int g = 0; g < G; ++g) red[wave][g][lane] = acc[g];
             __syncthreads();
             if (wave == 0) {
 #pragma unroll
-                for (int w2 = 1; w2 < NW; ++w2) acc += red[w2][lane];
+                for (int w2 = 1; w2 < NW; ++w2)
+#pragma unroll
+                    for (int g = 0; g < G; ++g) acc[g] += red[w2][g][lane];
             }
         }
         if (wave == 0 && yrow >= 0) {
-            // lane (r, j) holds rows 4 j .. 4 j + 3 of the tile for slot r
-            const int64_t n0 = 16 * t + 4 * j;
-            if (p.ws) {
-                float *dst = p.ws + yrow * p.N + n0;
-                *reinterpret_cast<v4f *>(dst) = acc;
-            } else {
-                float v[4] = {acc[0], acc[1], acc[2], acc[3]};
-                if (p.bias) {
-                    const uint16_t *bb = p.bias + n0;
-                    for (int i = 0; i < 4; ++i) v[i] += bf16_to_f32(bb[i]);
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (g >= ntiles) break;
+                // lane (r, j) holds rows 4 j .. 4 j + 3 of tile t0 + g for slot r
+                const int64_t n0 = 16 * (t0 + g) + 4 * j;
+                const v4f a = acc[g];
+                if (p.ws) {
+                    *reinterpret_cast<v4f *>(p.ws + yrow * p.N + n0) = a;
+                } else {
+                    float v[4] = {a[0], a[1], a[2], a[3]};
+                    if (p.bias) {
+                        const uint16_t *bb = p.bias + n0;
+                        for (int i = 0; i < 4; ++i) v[i] += bf16_to_f32(bb[i]);
+                    }
+                    v2u o = {bf16_bits(v[0]) | (bf16_bits(v[1]) << 16),
+                             bf16_bits(v[2]) | (bf16_bits(v[3]) << 16)};
+                    *reinterpret_cast<v2u *>(p.y + yrow * p.ldy + n0) = o;
                 }
-                v2u o = {bf16_bits(v[0]) | (bf16_bits(v[1]) << 16),
-                         bf16_bits(v[2]) | (bf16_bits(v[3]) << 16)};
-                *reinterpret_cast<v2u *>(p.y + yrow * p.ldy + n0) = o;
             }
         }
         if (NW > 1) __syncthreads();                 // red[] is reused by the next batch
@@ -268,27 +317,46 @@ __global__ void __launch_bounds__(256) moe_combine_kernel(int64_t T, int64_t top
     y[i] = (uint16_t)bf16_bits(s);
 }
 
-template <int ELEM, int LAYOUT, int ACT, bool MOE>
-static hipError_t launch_nw(const GemvArgs &a, int nw, dim3 grid, hipStream_t st) {
-    switch (nw) {
-    case 1: hipLaunchKernelGGL((gemv_kernel<ELEM, LAYOUT, ACT, MOE, 1>), grid, dim3(64), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((gemv_kernel<ELEM, LAYOUT, ACT, MOE, 2>), grid, dim3(128), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((gemv_kernel<ELEM, LAYOUT, ACT, MOE, 8>), grid, dim3(512), 0, st, a); break;
-    default: hipLaunchKernelGGL((gemv_kernel<ELEM, LAYOUT, ACT, MOE, 4>), grid, dim3(256), 0, st, a); break;
+template <int ELEM, int LAYOUT, int ACT, bool MOE, int NW, int G>
+static hipError_t launch_p(const GemvArgs &a, int chunk, dim3 grid, hipStream_t st) {
+    switch (chunk) {
+    case 2: hipLaunchKernelGGL((gemv_kernel<ELEM, LAYOUT, ACT, MOE, NW, 2, G>), grid, dim3(NW * 64), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((gemv_kernel<ELEM, LAYOUT, ACT, MOE, NW, 4, G>), grid, dim3(NW * 64), 0, st, a); break;
+    default: hipLaunchKernelGGL((gemv_kernel<ELEM, LAYOUT, ACT, MOE, NW, 8, G>), grid, dim3(NW * 64), 0, st, a); break;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_gemv(int elem, int layout, int act, bool moe, const GemvArgs &a, int nw,
-                       hipStream_t st) {
+template <int ELEM, int LAYOUT, int ACT, bool MOE, int G>
+static hipError_t launch_nw(const GemvArgs &a, int nw, int chunk, dim3 grid, hipStream_t st) {
+    switch (nw) {
+    case 1: return launch_p<ELEM, LAYOUT, ACT, MOE, 1, G>(a, chunk, grid, st);
+    case 2: return launch_p<ELEM, LAYOUT, ACT, MOE, 2, G>(a, chunk, grid, st);
+    case 8: return launch_p<ELEM, LAYOUT, ACT, MOE, 8, G>(a, chunk, grid, st);
+    default: return launch_p<ELEM, LAYOUT, ACT, MOE, 4, G>(a, chunk, grid, st);
+    }
+}
+
+template <int ELEM, int LAYOUT, int ACT, bool MOE>
+static hipError_t launch_g(const GemvArgs &a, const GemvShape &sh, hipStream_t st) {
     const int64_t T = a.N / 16;
-    // MoE: one extra group of T workgroups (unit e == E) zero-fills the rows of
+    const int64_t TG = (T + sh.tiles - 1) / sh.tiles;
+    // MoE: one extra group of TG workgroups (unit e == E) zero-fills the rows of
     // out-of-range ids; it exits at once when there are none
-    const dim3 grid = moe ? dim3((unsigned)((a.E + 1) * T))
-                          : dim3((unsigned)T, (unsigned)((a.rows + 15) / 16));
+    const dim3 grid = MOE ? dim3((unsigned)((a.E + 1) * TG))
+                          : dim3((unsigned)TG, (unsigned)((a.rows + 15) / 16));
+    switch (sh.tiles) {
+    case 2: return launch_nw<ELEM, LAYOUT, ACT, MOE, 2>(a, sh.nw, sh.chunk, grid, st);
+    case 4: return launch_nw<ELEM, LAYOUT, ACT, MOE, 4>(a, sh.nw, sh.chunk, grid, st);
+    default: return launch_nw<ELEM, LAYOUT, ACT, MOE, 1>(a, sh.nw, sh.chunk, grid, st);
+    }
+}
+
+hipError_t launch_gemv(int elem, int layout, int act, bool moe, const GemvArgs &a,
+                       const GemvShape &sh, hipStream_t st) {
 #define MX_GEMV_CASE(EL, LA, AC, MO)                                                     \
     if (elem == EL && layout == LA && act == AC && moe == MO)                              \
-        return launch_nw<EL, LA, AC, MO>(a, nw, grid, st);
+        return launch_g<EL, LA, AC, MO>(a, sh, st);
     MX_GEMV_CASE(E4M3, ROW32, ACT_MXFP8, false)
     MX_GEMV_CASE(E4M3, BLK32, ACT_MXFP8, false)
     MX_GEMV_CASE(E4M3, ROW32, ACT_BF16, false)

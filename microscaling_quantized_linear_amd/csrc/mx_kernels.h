@@ -49,8 +49,15 @@ hipError_t launch_pack(int elem, int layout, int64_t E, int64_t N, int64_t K, co
                        const void *codes, void *wp, void *cp, int *bad, hipStream_t stream);
 hipError_t launch_quant(int64_t M, int64_t K, const void *x, int64_t ldx, void *xq, int64_t ldq,
                         void *xcodes, int64_t ldc, int rule, hipStream_t stream);
-hipError_t launch_gemv(int elem, int layout, int act, bool moe, const GemvArgs &a, int nw,
-                       hipStream_t stream);
+// Launch shape of the GEMV: nw wavefronts per workgroup (1, 2, 4, 8) split
+// the 128-K steps; each issues the loads of `chunk` steps together (2, 4, 8);
+// a workgroup owns `tiles` 16-row weight tiles (1, 2, 4) that share the
+// activation loads.
+struct GemvShape {
+    int nw, chunk, tiles;
+};
+hipError_t launch_gemv(int elem, int layout, int act, bool moe, const GemvArgs &a,
+                       const GemvShape &shape, hipStream_t stream);
 hipError_t launch_moe_combine(int64_t T, int64_t topk, int64_t N, const float *ys,
                               const float *wts, void *y, hipStream_t stream);
 hipError_t launch_gemm(int layout, const GemmArgs &a, hipStream_t stream);
