@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None,
                     help="run one workload only (gemv16, gemv1, gemv4, a16_c1, a16_c3, moe, gemm)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch without HIP graphs (for hardware-counter runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 64 MiB device copy 20 times (counter calibration)")
     return ap.parse_args()
 
 
@@ -78,12 +82,20 @@ class GraphTimer:
                 fn(i)
         return g
 
+    eager = False
+
     def time(self, fn, steps, warmup):
         """ms per call of fn(i), over `steps` calls replayed back to back."""
         torch = self.torch
         for i in range(2):
             fn(i)                      # eager first calls (one-time setup)
         torch.cuda.synchronize()
+        if GraphTimer.eager:           # counter runs: plain launches, rough timing
+            t = time.perf_counter()
+            for i in range(steps):
+                fn(i)
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t) * 1e3 / steps
         gw = self._graph(fn, max(warmup, 1))
         gt = self._graph(fn, steps)
         gw.replay()
@@ -273,6 +285,15 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
     K, W = args.steps, args.warmup
+    if args.copy_calibration:
+        a = torch.empty(64 << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(20):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": a.numel(), "launches": 20}))
+        return
+    GraphTimer.eager = args.eager
 
     only = args.only
     want = (lambda n: only is None or only == n)

@@ -20,22 +20,30 @@
 namespace mx {
 
 constexpr int kBM = 256;           // tokens per workgroup
-constexpr int kXPitch = 144;       // LDS bytes per activation row (128 + 16)
 
+// Per LDS buffer: the step's weight chunks (2 NTW x 2 KB, W-T16 as stored) then
+// the activation tile in MFMA fragment order (16 chunks of 16 rows x 128 K:
+// byte 1024 h + 16 l of chunk mt holds row 16 mt + l%16, K 64 h + 16 (l/16)).
 template <int NTW>
 struct GemmSmem {
-    static constexpr int kWBytes = 2 * NTW * 2048;        // weight chunks per step
-    static constexpr int kXBytes = kBM * kXPitch;
+    static constexpr int kWBytes = 2 * NTW * 2048;
+    static constexpr int kXBytes = kBM / 16 * 2048;
     static constexpr int kBuf = kWBytes + kXBytes;
-    static constexpr int kTotal = 2 * kBuf;
+    static constexpr int kDma = kBuf / 1024;              // 1 KB DMA loads per step
 };
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 template <int LAYOUT, int NTW>
 __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     using SM = GemmSmem<NTW>;
+    // two distinct buffers: the compiler can then tell the DMA into one from
+    // the operand reads of the other and waits only where it must
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[SM::kBuf];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[SM::kBuf];
     constexpr int BN = 2 * NTW * 16;
-    const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+    const int tid = threadIdx.x, lane = tid % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int r = lane % 16, j = lane / 16;
     const int wn = wave % 2, wm = wave / 2;
     const int64_t Kp = (p.K + 127) / 128 * 128, S = Kp / 128, T = p.N / 16, Q = (S + 3) / 4;
@@ -43,7 +51,7 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
 
     // tile order: consecutive workgroups go to different XCDs; give each XCD
     // a band of N tiles so the weight panels it streams stay in its L2
-    const int64_t tiles_n = (p.N + BN - 1) / BN, tiles_m = (p.M + kBM - 1) / kBM;
+    const int64_t tiles_n = (p.N + BN - 1) / BN;
     int64_t bid = blockIdx.x, tn, tm;
     if (tiles_n % 8 == 0) {
         const int64_t xcd = bid % 8, local = bid / 8, per = tiles_n / 8;
@@ -63,54 +71,69 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
         make_rsrc(p.codes, LAYOUT == ROW32 ? (uint32_t)(T * Q * 256)
                                            : (uint32_t)((p.N / 32) * (Kp / 32)));
 
-    // ---- global -> register staging for one step ----
-    v4u wst[NTW], xst[8];
-    auto issue_loads = [&](int64_t s) {
+    // ---- DMA assignment: wave w issues weight chunk-halves w, w + 4, ... and
+    // activation chunk-halves w, w + 4, ...; chunk-half i lands at i KB.
+    // Offsets of out-of-range loads get bit 31 set (every resource is below
+    // 2 GiB, so those lanes read zeros); no branches in the loop body.
+    constexpr int kWq = NTW;                              // 4 NTW weight loads / 4 waves
+    constexpr int kXq = 8;                                // 32 activation loads / 4 waves
+    uint32_t wbase[kWq], xbase[kXq], xkmax[kXq];
 #pragma unroll
-        for (int q = 0; q < NTW; ++q) {
-            const int64_t c = 2 * q + tid / 128;           // chunk within the tile column
-            const int64_t t = t0 + c;
-            const uint32_t off = t < T ? (uint32_t)((t * S + s) * 2048 + 16 * (tid % 128)) : kOOB;
-            wst[q] = load16<kNT>(wr, off);
-        }
+    for (int q = 0; q < kWq; ++q) {
+        const int i = wave + 4 * q, c = i / 2, h = i % 2;
+        const int64_t t = t0 + c;
+        wbase[q] = t < T ? (uint32_t)(t * S * 2048 + 1024 * h + 16 * lane) : kOOB;
+    }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int64_t row = m0 + 32 * q + tid / 8;
-            const int64_t k = 128 * s + 16 * (tid % 8);
-            const uint32_t off = (row < p.M && k < p.K) ? (uint32_t)(row * p.ldq + k) : kOOB;
-            xst[q] = load16(xr, off);
-        }
+    for (int q = 0; q < kXq; ++q) {
+        const int i = wave + 4 * q, mc = i / 2, h = i % 2;
+        const int64_t row = m0 + 16 * mc + r, k = 64 * h + 16 * j;
+        xbase[q] = row < p.M ? (uint32_t)(row * p.ldq + k) : kOOB;
+        xkmax[q] = (uint32_t)((p.K - k + 127) / 128);     // steps with 128 s + k < K
+    }
+    auto dma = [&](uint8_t *buf, int64_t s) {
+        const uint32_t su = (uint32_t)s, past = su >= (uint32_t)S ? kOOB : 0u;
+#pragma unroll
+        for (int q = 0; q < kWq; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                wr, (lds_void *)(buf + (wave + 4 * q) * 1024), 16,
+                (int)((wbase[q] + su * 2048u) | past), 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < kXq; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xr, (lds_void *)(buf + SM::kWBytes + (wave + 4 * q) * 1024), 16,
+                (int)((xbase[q] + su * 128u) | (su >= xkmax[q] ? kOOB : 0u)), 0, 0, 0);
     };
-    auto store_lds = [&](int buf) {
-        uint8_t *wb = smem + buf * SM::kBuf;
-        uint8_t *xb = wb + SM::kWBytes;
-#pragma unroll
-        for (int q = 0; q < NTW; ++q)
-            *reinterpret_cast<v4u *>(wb + q * 4096 + 16 * tid) = wst[q];
-#pragma unroll
-        for (int q = 0; q < 8; ++q)
-            *reinterpret_cast<v4u *>(xb + (32 * q + tid / 8) * kXPitch + 16 * (tid % 8)) = xst[q];
+
+    // ---- per-lane scales of one step (raw; byte selected at use) ----
+    struct Scales {
+        uint32_t w[NTW], x[8];
     };
-    // ---- per-lane scales of one step ----
-    uint32_t sw[NTW], sx[8];
-    auto load_scales = [&](int64_t s, uint32_t *w_out, uint32_t *x_out) {
+    uint32_t cwbase[NTW], cxbase[8];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+        const int64_t t = t0 + wn * NTW + nt;
+        if (LAYOUT == ROW32)
+            cwbase[nt] = t < T ? (uint32_t)(t * Q * 256 + 4 * lane) : kOOB;
+        else
+            cwbase[nt] = t < T ? (uint32_t)(((16 * t) / 32) * (Kp / 32)) : kOOB;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+        const int64_t row = m0 + wm * 128 + 16 * mt + r;
+        cxbase[mt] = row < p.M ? (uint32_t)(row * p.ldc + j) : kOOB;
+    }
+    auto load_scales = [&](int64_t s, Scales &out) {
+        const uint32_t su = (uint32_t)s, past = su >= (uint32_t)S ? kOOB : 0u;
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
-            const int64_t t = t0 + wn * NTW + nt;
-            if (LAYOUT == ROW32) {
-                const uint32_t off = t < T ? (uint32_t)((t * Q + s / 4) * 256 + 4 * lane) : kOOB;
-                w_out[nt] = byte_of(load4(cr, off), (uint32_t)(s % 4));
-            } else {
-                const uint32_t off = t < T ? (uint32_t)(((16 * t) / 32) * (Kp / 32) + 4 * s) : kOOB;
-                w_out[nt] = byte_of(load4(cr, off), (uint32_t)j);
-            }
+            const uint32_t off = LAYOUT == ROW32 ? cwbase[nt] + (su / 4) * 256u : cwbase[nt] + 4u * su;
+            out.w[nt] = load4(cr, off | past);
         }
+        // block 4 s + j exists while 4 s + j < K / 32
+        const uint32_t xpast = (4 * su + (uint32_t)j) >= (uint32_t)KB ? kOOB : 0u;
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const int64_t row = m0 + wm * 128 + 16 * mt + r;
-            const int64_t blk = 4 * s + j;
-            x_out[mt] = load1(xcr, (row < p.M && blk < KB) ? (uint32_t)(row * p.ldc + blk) : kOOB);
-        }
+        for (int mt = 0; mt < 8; ++mt) out.x[mt] = load1(xcr, (cxbase[mt] + 4u * su) | xpast);
     };
 
     v4f acc[NTW][8];
@@ -119,45 +142,47 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
 #pragma unroll
         for (int b = 0; b < 8; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    issue_loads(0);
-    load_scales(0, sw, sx);
-    store_lds(0);
-    __syncthreads();
-
-    for (int64_t s = 0; s < S; ++s) {
-        const int cur = (int)(s & 1);
-        uint32_t swn[NTW], sxn[8];
-        const bool more = s + 1 < S;
-        if (more) {
-            issue_loads(s + 1);
-            load_scales(s + 1, swn, sxn);
-        }
-        const uint8_t *wb = smem + cur * SM::kBuf;
-        const uint8_t *xb = wb + SM::kWBytes;
+    // one 128-K step: DMA of step s + 1 into `nxt`, then the MFMAs of step s
+    // from `cur`; the scales of step s + 1 load into `sn` while `sc` is used
+    auto step = [&](uint8_t *cur, uint8_t *nxt, int64_t s, const Scales &sc, Scales &sn) {
+        dma(nxt, s + 1);
+        load_scales(s + 1, sn);
+        __builtin_amdgcn_sched_barrier(0);
         v8i bf[8];
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-            const uint8_t *rowp = xb + (wm * 128 + 16 * mt + r) * kXPitch;
-            bf[mt] = cat8(*reinterpret_cast<const v4u *>(rowp + 16 * j),
-                          *reinterpret_cast<const v4u *>(rowp + 64 + 16 * j));
+            const uint8_t *cp = cur + SM::kWBytes + (wm * 8 + mt) * 2048;
+            bf[mt] = cat8(*reinterpret_cast<const v4u *>(cp + 16 * lane),
+                          *reinterpret_cast<const v4u *>(cp + 1024 + 16 * lane));
+        }
+        v8i af[NTW];
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+            const uint8_t *cp = cur + (wn * NTW + nt) * 2048;
+            af[nt] = cat8(*reinterpret_cast<const v4u *>(cp + 16 * lane),
+                          *reinterpret_cast<const v4u *>(cp + 1024 + 16 * lane));
         }
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
-            const uint8_t *cp = wb + (wn * NTW + nt) * 2048;
-            const v8i af = cat8(*reinterpret_cast<const v4u *>(cp + 16 * lane),
-                                *reinterpret_cast<const v4u *>(cp + 1024 + 16 * lane));
+            const int swv = (int)(LAYOUT == ROW32 ? byte_of(sc.w[nt], (uint32_t)(s % 4))
+                                                  : byte_of(sc.w[nt], (uint32_t)j));
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt)
-                acc[nt][mt] = mfma_fp8_scaled(af, bf[mt], acc[nt][mt], (int)sw[nt], (int)sx[mt]);
+                acc[nt][mt] = mfma_fp8_scaled(af[nt], bf[mt], acc[nt][mt], swv, (int)sc.x[mt]);
         }
-        if (more) {
-            store_lds(cur ^ 1);
-#pragma unroll
-            for (int nt = 0; nt < NTW; ++nt) sw[nt] = swn[nt];
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt) sx[mt] = sxn[mt];
-        }
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
+    };
+
+    Scales sA, sB;
+    dma(lds0, 0);
+    load_scales(0, sA);
+    __syncthreads();
+    // two steps per iteration so each buffer is a fixed LDS object; a step
+    // at or past S reads zeros (and adds nothing)
+    for (int64_t s = 0; s < S; s += 2) {
+        step(lds0, lds1, s, sA, sB);
+        step(lds1, lds0, s + 1, sB, sA);
     }
 
     // ---- epilogue: lane (r, j) of tile (nt, mt) holds n = 4 j .. 4 j + 3, m = r ----
@@ -184,20 +209,7 @@ template <int LAYOUT, int NTW>
 static hipError_t launch_ntw(const GemmArgs &a, hipStream_t st) {
     constexpr int BN = 2 * NTW * 16;
     const int64_t tiles = ((a.N + BN - 1) / BN) * ((a.M + kBM - 1) / kBM);
-    const int smem = GemmSmem<NTW>::kTotal;
-    // the LDS-size attribute is set once per device (outside any graph capture
-    // that follows the first call)
-    static bool attr_done[64] = {};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64 || !attr_done[dev]) {
-        e = hipFuncSetAttribute((const void *)gemm_w8a8_kernel<LAYOUT, NTW>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-        if (e != hipSuccess) return e;
-        if (dev >= 0 && dev < 64) attr_done[dev] = true;
-    }
-    hipLaunchKernelGGL((gemm_w8a8_kernel<LAYOUT, NTW>), dim3((unsigned)tiles), dim3(256), smem, st,
+    hipLaunchKernelGGL((gemm_w8a8_kernel<LAYOUT, NTW>), dim3((unsigned)tiles), dim3(256), 0, st,
                        a);
     return hipGetLastError();
 }
