@@ -231,13 +231,15 @@ def bench_gemm(torch, mx, g, wl, steps, warmup):
     xq = torch.empty((M, K), dtype=torch.uint8, device=g.DEV)
     xc = torch.empty((M, K // 32), dtype=torch.uint8, device=g.DEV)
     y = torch.empty((M, N), dtype=torch.int16, device=g.DEV)
+    need = mx.mx_linear_workspace(0, 1, N, K, M, mx.MX_ACT_MXFP8, 1)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=g.DEV)
 
     def step(i):
         mx.mx_quant_act(M, K, x, K, xq, K, xc, K // 32, mx.MX_RULE_OCP)
 
     def kernel(i):
         mx.mx_linear(0, 1, N, K, wp, cp, M, mx.MX_ACT_MXFP8, 0, None, 0, xq, K, xc, K // 32,
-                     None, y, N, None, 0)
+                     None, y, N, ws, need)
 
     ms_step, ms_k = GraphTimer(torch).run(step, kernel, steps, warmup)
     flop = 2.0 * M * N * K

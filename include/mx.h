@@ -83,7 +83,10 @@ typedef enum { MX_ACT_BF16 = 0, MX_ACT_MXFP8 = 1 } mx_act;
  * Packed codes:
  *   ROW32: 256 bytes per (e, t, q) at ((e T + t) Q + q) * 256;
  *          byte 4 l + u = code[e N + 16 t + r][4 (4 q + u) + j].
- *   BLK32: row-major [E N / 32, Kp / 32].
+ *   BLK32: 16 bytes per (32-row group R, q) at (R Q + q) * 16, R < E N / 32;
+ *          byte 4 j + u = code[R][4 (4 q + u) + j].
+ * Each lane group j reads one dword per quad of steps, whose byte u is the
+ * code of step 4 q + u: the scaled MFMA's byte select picks it directly.
  */
 
 /* Sizes of the packed buffers for a weight of E experts x [N, K].
@@ -118,9 +121,12 @@ mx_status mx_quant_act(int64_t M, int64_t K, const void *x, int64_t ldx,
                        void *xq, int64_t ldq, void *xcodes, int64_t ldc,
                        int rule, mx_stream_t stream);
 
-/* Workspace bytes mx_linear needs for these arguments (0 when none):
- * M * Kp + M * Kp / 32 (+ alignment) when act == MX_ACT_MXFP8 and the
- * activation is quantized inside the call (pass prequantized = 0). */
+/* Workspace bytes mx_linear needs for these arguments (0 when none), for
+ * act == MX_ACT_MXFP8:
+ *   M * Kp + M * Kp / 32 (each rounded up to 256) when the activation is
+ *   quantized inside the call (prequantized = 0), plus
+ *   ceil(M / 16) * Q * 256 when M > 64 (the prefill GEMM path restages the
+ *   row-major activation codes into 16-row tiles, pre-quantized or not). */
 mx_status mx_linear_workspace(int elem, int layout, int64_t N, int64_t K,
                               int64_t M, int act, int prequantized,
                               size_t *bytes);
@@ -139,6 +145,10 @@ mx_status mx_linear_workspace(int elem, int layout, int64_t N, int64_t K,
  *   xcodes (device) [M, ldc], ldc >= K / 32
  *   bias (device, nullable) bf16 [N]
  *   y   (device) bf16 [M, ldy]: 16-byte aligned, ldy % 8 == 0, ldy >= N
+ *   ws  (device) at least mx_linear_workspace's bytes, 16-byte aligned
+ *       (may be NULL when that is 0); its contents on return are unspecified
+ * The call is asynchronous on `stream`, allocates nothing and may be
+ * captured in a graph.
  * Built combinations: E4M3 x {ROW32, BLK32} x {BF16, MXFP8};
  * E2M1 x ROW32 x BF16.  Others: MX_ERR_UNSUPPORTED. */
 mx_status mx_linear(int elem, int layout, int64_t N, int64_t K,

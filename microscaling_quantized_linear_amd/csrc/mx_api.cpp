@@ -23,6 +23,9 @@ using mx::ROW32;
 
 constexpr int64_t kMaxRsrc = (int64_t(1) << 31) - 1;   // 32-bit buffer offsets
 
+// largest M served by the decode GEMV for W8A8; above it the GEMM runs
+constexpr int64_t kGemvMaxM = 64;
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 int64_t padded_k(int64_t K) { return (K + 127) / 128 * 128; }
 
@@ -85,9 +88,6 @@ mx::GemvShape gemv_shape(int64_t S, bool moe) {
     return g;
 }
 
-// largest M served by the decode GEMV for W8A8; above it the GEMM runs
-constexpr int64_t kGemvMaxM = 64;
-
 }  // namespace
 
 extern "C" {
@@ -119,7 +119,7 @@ mx_status mx_packed_sizes(int elem, int layout, int64_t E, int64_t N, int64_t K,
     if (st != MX_OK) return st;
     const int64_t Kp = padded_k(K), S = Kp / 128, Q = (S + 3) / 4;
     *w_bytes = (size_t)(E * N * (elem == E4M3 ? Kp : Kp / 2));
-    *code_bytes = (size_t)(layout == ROW32 ? E * (N / 16) * Q * 256 : E * (N / 32) * (Kp / 32));
+    *code_bytes = (size_t)(layout == ROW32 ? E * (N / 16) * Q * 256 : E * (N / 32) * Q * 16);
     return MX_OK;
 }
 
@@ -168,9 +168,12 @@ mx_status mx_linear_workspace(int elem, int layout, int64_t N, int64_t K, int64_
     if (M < 1) return MX_ERR_SHAPE;
     if (act != ACT_BF16 && act != ACT_MXFP8) return MX_ERR_UNSUPPORTED;
     *bytes = 0;
-    if (act == ACT_MXFP8 && !prequantized) {
+    if (act == ACT_MXFP8) {
         const int64_t Kp = padded_k(K);
-        *bytes = (size_t)(M * Kp + 256 + M * (Kp / 32));
+        int64_t b = 0;
+        if (!prequantized) b += (M * Kp + 255) / 256 * 256 + (M * (Kp / 32) + 255) / 256 * 256;
+        if (M > kGemvMaxM) b += mx::act_codes_t16_bytes(M, K);   // GEMM code staging
+        *bytes = (size_t)b;
     }
     return MX_OK;
 }
@@ -215,10 +218,12 @@ mx_status mx_linear(int elem, int layout, int64_t N, int64_t K, const void *w_pa
     const uint8_t *aq = static_cast<const uint8_t *>(xq);
     const uint8_t *ac = static_cast<const uint8_t *>(xcodes);
     int64_t lq = ldq, lc = ldc;
+    uint8_t *wsp = static_cast<uint8_t *>(ws);
     if (act == ACT_MXFP8 && !preq) {
         // quantize into the workspace: e4m3 [M, Kp] then codes [M, Kp/32]
-        uint8_t *q = static_cast<uint8_t *>(ws);
-        uint8_t *c = q + ((M * Kp + 255) / 256) * 256;
+        uint8_t *q = wsp;
+        uint8_t *c = q + (M * Kp + 255) / 256 * 256;
+        wsp = c + (M * (Kp / 32) + 255) / 256 * 256;
         lq = Kp;
         lc = Kp / 32;
         if ((st = launched(mx::launch_quant(M, K, x, ldx, q, lq, c, lc, rule, s))) != MX_OK)
@@ -227,6 +232,8 @@ mx_status mx_linear(int elem, int layout, int64_t N, int64_t K, const void *w_pa
         ac = c;
     }
     if (gemm) {
+        // restage the activation codes for the GEMM's per-lane scale loads
+        if ((st = launched(mx::launch_act_codes_t16(M, K, ac, lc, wsp, s))) != MX_OK) return st;
         mx::GemmArgs g{};
         g.w = static_cast<const uint8_t *>(w_packed);
         g.codes = static_cast<const uint8_t *>(codes_packed);
@@ -235,8 +242,7 @@ mx_status mx_linear(int elem, int layout, int64_t N, int64_t K, const void *w_pa
         g.M = M;
         g.xq = aq;
         g.ldq = lq;
-        g.xcodes = ac;
-        g.ldc = lc;
+        g.xct = wsp;
         g.bias = static_cast<const uint16_t *>(bias);
         g.y = static_cast<uint16_t *>(y);
         g.ldy = ldy;

@@ -93,6 +93,12 @@ __device__ inline v4f mfma_fp8_scaled(v8i a, v8i b, v4f c, int sa, int sb) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
 
+// the same with the scale bytes picked by opsel (byte U of sa and of sb)
+template <int U>
+__device__ inline v4f mfma_fp8_scaled_sel(v8i a, v8i b, v4f c, int sa, int sb) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, U, sa, U, sb);
+}
+
 __device__ inline v8i cat8(v4u lo, v4u hi) {
     v8i r = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
              (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};

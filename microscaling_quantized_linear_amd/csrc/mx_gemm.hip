@@ -17,6 +17,8 @@
 #include "mx_device.h"
 #include "mx_kernels.h"
 
+#include <type_traits>
+
 namespace mx {
 
 constexpr int kBM = 256;           // tokens per workgroup
@@ -66,10 +68,10 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
 
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w, (uint32_t)(T * S * 2048));
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.xq, (uint32_t)(p.M * p.ldq));
-    const __amdgpu_buffer_rsrc_t xcr = make_rsrc(p.xcodes, (uint32_t)(p.M * p.ldc));
+    const __amdgpu_buffer_rsrc_t xcr = make_rsrc(p.xct, (uint32_t)act_codes_t16_bytes(p.M, p.K));
     const __amdgpu_buffer_rsrc_t cr =
         make_rsrc(p.codes, LAYOUT == ROW32 ? (uint32_t)(T * Q * 256)
-                                           : (uint32_t)((p.N / 32) * (Kp / 32)));
+                                           : (uint32_t)((p.N / 32) * Q * 16));
 
     // ---- DMA assignment: wave w issues weight chunk-halves w, w + 4, ... and
     // activation chunk-halves w, w + 4, ...; chunk-half i lands at i KB.
@@ -105,8 +107,9 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
                 (int)((xbase[q] + su * 128u) | (su >= xkmax[q] ? kOOB : 0u)), 0, 0, 0);
     };
 
-    // ---- per-lane scales of one step (raw; byte selected at use) ----
-    struct Scales {
+    // ---- per-lane scale dwords of one quad of four steps: byte u of each
+    // dword is step 4 q + u's code, picked by the MFMA's opsel ----
+    struct QScales {
         uint32_t w[NTW], x[8];
     };
     uint32_t cwbase[NTW], cxbase[8];
@@ -116,24 +119,20 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
         if (LAYOUT == ROW32)
             cwbase[nt] = t < T ? (uint32_t)(t * Q * 256 + 4 * lane) : kOOB;
         else
-            cwbase[nt] = t < T ? (uint32_t)(((16 * t) / 32) * (Kp / 32)) : kOOB;
+            cwbase[nt] = t < T ? (uint32_t)(((16 * t) / 32) * Q * 16 + 4 * j) : kOOB;
     }
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
-        const int64_t row = m0 + wm * 128 + 16 * mt + r;
-        cxbase[mt] = row < p.M ? (uint32_t)(row * p.ldc + j) : kOOB;
+        const int64_t row0 = m0 + wm * 128 + 16 * mt;     // XC-T16 tile of 16 rows
+        cxbase[mt] = row0 < p.M ? (uint32_t)((row0 / 16) * Q * 256 + 4 * lane) : kOOB;
     }
-    auto load_scales = [&](int64_t s, Scales &out) {
-        const uint32_t su = (uint32_t)s, past = su >= (uint32_t)S ? kOOB : 0u;
+    auto load_qscales = [&](int64_t q, QScales &out) {
+        const uint32_t qu = (uint32_t)q, past = qu >= (uint32_t)Q ? kOOB : 0u;
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-            const uint32_t off = LAYOUT == ROW32 ? cwbase[nt] + (su / 4) * 256u : cwbase[nt] + 4u * su;
-            out.w[nt] = load4(cr, off | past);
-        }
-        // block 4 s + j exists while 4 s + j < K / 32
-        const uint32_t xpast = (4 * su + (uint32_t)j) >= (uint32_t)KB ? kOOB : 0u;
+        for (int nt = 0; nt < NTW; ++nt)
+            out.w[nt] = load4(cr, (cwbase[nt] + qu * (LAYOUT == ROW32 ? 256u : 16u)) | past);
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) out.x[mt] = load1(xcr, (cxbase[mt] + 4u * su) | xpast);
+        for (int mt = 0; mt < 8; ++mt) out.x[mt] = load4(xcr, (cxbase[mt] + qu * 256u) | past);
     };
 
     v4f acc[NTW][8];
@@ -142,11 +141,11 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
 #pragma unroll
         for (int b = 0; b < 8; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
 
-    // one 128-K step: DMA of step s + 1 into `nxt`, then the MFMAs of step s
-    // from `cur`; the scales of step s + 1 load into `sn` while `sc` is used
-    auto step = [&](uint8_t *cur, uint8_t *nxt, int64_t s, const Scales &sc, Scales &sn) {
+    // one 128-K step, step u of its quad: DMA of step s + 1 into `nxt`, then
+    // the MFMAs of step s from `cur` with the quad's scales `sc`
+    auto step = [&](uint8_t *cur, uint8_t *nxt, int64_t s, const QScales &sc, auto uconst) {
+        constexpr int U = decltype(uconst)::value;
         dma(nxt, s + 1);
-        load_scales(s + 1, sn);
         __builtin_amdgcn_sched_barrier(0);
         v8i bf[8];
 #pragma unroll
@@ -163,26 +162,38 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
                           *reinterpret_cast<const v4u *>(cp + 1024 + 16 * lane));
         }
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-            const int swv = (int)(LAYOUT == ROW32 ? byte_of(sc.w[nt], (uint32_t)(s % 4))
-                                                  : byte_of(sc.w[nt], (uint32_t)j));
+        for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt)
-                acc[nt][mt] = mfma_fp8_scaled(af[nt], bf[mt], acc[nt][mt], swv, (int)sc.x[mt]);
-        }
+                acc[nt][mt] = mfma_fp8_scaled_sel<U>(af[nt], bf[mt], acc[nt][mt], (int)sc.w[nt],
+                                                     (int)sc.x[mt]);
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
     };
+    using U0 = std::integral_constant<int, 0>;
+    using U1 = std::integral_constant<int, 1>;
+    using U2 = std::integral_constant<int, 2>;
+    using U3 = std::integral_constant<int, 3>;
 
-    Scales sA, sB;
+    QScales qa, qb;
     dma(lds0, 0);
-    load_scales(0, sA);
+    load_qscales(0, qa);
     __syncthreads();
-    // two steps per iteration so each buffer is a fixed LDS object; a step
-    // at or past S reads zeros (and adds nothing)
-    for (int64_t s = 0; s < S; s += 2) {
-        step(lds0, lds1, s, sA, sB);
-        step(lds1, lds0, s + 1, sB, sA);
+    // eight steps (two quads) per iteration: each LDS buffer is a fixed object
+    // and the two scale sets alternate without copies; a step at or past S
+    // reads zeros and adds nothing
+    for (int64_t s = 0; s < S; s += 8) {
+        const int64_t q = s / 4;
+        load_qscales(q + 1, qb);
+        step(lds0, lds1, s + 0, qa, U0{});
+        step(lds1, lds0, s + 1, qa, U1{});
+        step(lds0, lds1, s + 2, qa, U2{});
+        step(lds1, lds0, s + 3, qa, U3{});
+        load_qscales(q + 2, qa);
+        step(lds0, lds1, s + 4, qb, U0{});
+        step(lds1, lds0, s + 5, qb, U1{});
+        step(lds0, lds1, s + 6, qb, U2{});
+        step(lds1, lds0, s + 7, qb, U3{});
     }
 
     // ---- epilogue: lane (r, j) of tile (nt, mt) holds n = 4 j .. 4 j + 3, m = r ----

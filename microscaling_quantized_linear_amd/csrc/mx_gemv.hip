@@ -37,7 +37,7 @@ template <int G>
 struct StepA16 {
     v4u a0[G], a1[G];     // e4m3: two halves; e2m1: a0 only
     v4u x0, x1, x2, x3;   // bf16 activations of the four MFMAs
-    uint32_t cw[G];
+    uint32_t cw[G], cw2[G];
 };
 
 // G: weight tiles per workgroup.  A wavefront's activation fragment of a step
@@ -101,10 +101,10 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
     if (LAYOUT == ROW32)
         cr = make_rsrc(p.codes + (e * T + t0) * Q * 256, (uint32_t)(ntiles * Q * 256));
     else
-        cr = make_rsrc(p.codes, (uint32_t)(p.E * (p.N / 32) * (Kp / 32)));
-    uint32_t crow[G];                                // BLK32: code row offset of each tile
+        cr = make_rsrc(p.codes, (uint32_t)(p.E * (p.N / 32) * Q * 16));
+    uint32_t crow[G];                                // BLK32: code offset of each tile's row group
 #pragma unroll
-    for (int g = 0; g < G; ++g) crow[g] = (uint32_t)(((e * p.N + 16 * (t0 + g)) / 32) * (Kp / 32));
+    for (int g = 0; g < G; ++g) crow[g] = (uint32_t)(((e * p.N + 16 * (t0 + g)) / 32) * Q * 16);
     const int64_t xelt = ACT == ACT_MXFP8 ? 1 : 2;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.x, (uint32_t)(p.xrows * p.ldx * xelt));
     const __amdgpu_buffer_rsrc_t xcr =
@@ -118,10 +118,13 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
     auto woff = [&](int g, int64_t s, bool in) -> uint32_t {
         return in ? (uint32_t)((g * S + s) * CHUNK + 16 * lane) : kOOB;
     };
-    auto coff = [&](int g, int64_t s, bool in) -> uint32_t {
+    // the dword holding this step's code of the lane's row for lane group jj
+    // (byte s % 4 of it): ROW32 the lane's own C-T16 dword, BLK32 dword jj of
+    // the row group's 16-byte quad
+    auto coff = [&](int g, int64_t s, bool in, int jj) -> uint32_t {
         if (!in) return kOOB;
         if (LAYOUT == ROW32) return (uint32_t)((g * Q + s / 4) * 256 + 4 * lane);
-        return crow[g] + (uint32_t)(4 * s);
+        return crow[g] + (uint32_t)((s / 4) * 16 + 4 * jj);
     };
 
     for (int64_t bi = b_first; bi < b_last; ++bi) {
@@ -164,15 +167,14 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
                 const int64_t blk = 4 * s + j;                       // scale block of lane group j
                 st.cx = load1(xcr, in && live && blk < KB ? cxbase + (uint32_t)blk : kOOB);
 #pragma unroll
-                for (int g = 0; g < G; ++g) st.cw[g] = load4(cr, coff(g, s, in));
+                for (int g = 0; g < G; ++g) st.cw[g] = load4(cr, coff(g, s, in, j));
                 return st;
             };
             auto compute = [&](const StepW8A8<G> &st, int64_t s) {
                 const v8i b = cat8(st.b0, st.b1);
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    const uint32_t sw = LAYOUT == ROW32 ? byte_of(st.cw[g], (uint32_t)(s % 4))
-                                                        : byte_of(st.cw[g], (uint32_t)j);
+                    const uint32_t sw = byte_of(st.cw[g], (uint32_t)(s % 4));
                     acc[g] = mfma_fp8_scaled(cat8(st.a0[g], st.a1[g]), b, acc[g], (int)sw,
                                              (int)st.cx);
                 }
@@ -218,7 +220,14 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
                     st.x3 = load16(xr, v0 ? xbase + (uint32_t)(2 * k0 + 48) : kOOB);
                 }
 #pragma unroll
-                for (int g = 0; g < G; ++g) st.cw[g] = load4(cr, coff(g, s, in));
+                for (int g = 0; g < G; ++g) {
+                    if (ELEM == E4M3 && LAYOUT == BLK32) {
+                        st.cw[g] = load4(cr, coff(g, s, in, j / 2));
+                        st.cw2[g] = load4(cr, coff(g, s, in, 2 + j / 2));
+                    } else {
+                        st.cw[g] = load4(cr, coff(g, s, in, j));
+                    }
+                }
                 return st;
             };
             auto compute = [&](const StepA16<G> &st, int64_t s) {
@@ -233,8 +242,8 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
                             c0 = byte_of((uint32_t)__shfl((int)st.cw[g], 16 * (j / 2) + r), u);
                             c1 = byte_of((uint32_t)__shfl((int)st.cw[g], 16 * (2 + j / 2) + r), u);
                         } else {
-                            c0 = byte_of(st.cw[g], (uint32_t)(j / 2));
-                            c1 = byte_of(st.cw[g], (uint32_t)(2 + j / 2));
+                            c0 = byte_of(st.cw[g], (uint32_t)(s % 4));
+                            c1 = byte_of(st.cw2[g], (uint32_t)(s % 4));
                         }
                         const float f0 = code_as_scale(c0), f1 = code_as_scale(c1);
                         v4f c = acc[g];
@@ -244,8 +253,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
                         c = mfma_bf16(dec8_e4m3(st.a1[g][2], st.a1[g][3], f1), as_bf16x8(st.x3), c);
                         acc[g] = c;
                     } else {
-                        const uint32_t cc = LAYOUT == ROW32 ? byte_of(st.cw[g], (uint32_t)(s % 4))
-                                                            : byte_of(st.cw[g], (uint32_t)j);
+                        const uint32_t cc = byte_of(st.cw[g], (uint32_t)(s % 4));
                         const float f = code_as_scale(cc);
                         v4f c = acc[g];
                         c = mfma_bf16(dec8_e2m1(st.a0[g][0], f), as_bf16x8(st.x0), c);

@@ -38,12 +38,19 @@ struct GemmArgs {
     int64_t N, K, M;
     const uint8_t *xq;
     int64_t ldq;
-    const uint8_t *xcodes;
-    int64_t ldc;
+    const uint8_t *xct;      // activation codes in XC-T16 order (act_codes_t16)
     const uint16_t *bias;
     uint16_t *y;
     int64_t ldy;
 };
+
+// bytes of the XC-T16 activation-code staging for M rows
+__host__ __device__ inline int64_t act_codes_t16_bytes(int64_t M, int64_t K) {
+    const int64_t S = (K + 127) / 128, Q = (S + 3) / 4;
+    return (M + 15) / 16 * Q * 256;
+}
+hipError_t launch_act_codes_t16(int64_t M, int64_t K, const void *xc, int64_t ldc, void *out,
+                                hipStream_t stream);
 
 hipError_t launch_pack(int elem, int layout, int64_t E, int64_t N, int64_t K, const void *w,
                        const void *codes, void *wp, void *cp, int *bad, hipStream_t stream);

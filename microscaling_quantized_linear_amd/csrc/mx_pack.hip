@@ -5,7 +5,8 @@
 // fp4_tile_major (16-row tiles x 128-K steps, each 16-byte load of a
 // wavefront reading 1 KB that is contiguous); the code staging follows
 // [weights942] codes_tile_rounds (a lane group reads its rows' codes from one
-// line) with the per-lane dwords of [a16w4] scale_loads.  Padding to
+// line) with the per-lane dwords of [a16w4] scale_loads; BLK32 codes get the
+// same dword-per-lane-group, byte-per-step staging.  Padding to
 // Kp = 128 * ceil(K / 128) uses zero bytes and code 128 ([weights942]
 // dense_copy).
 #include "mx_device.h"
@@ -70,7 +71,11 @@ __global__ void __launch_bounds__(256) pack_codes_kernel(
         }
         reinterpret_cast<uint32_t *>(cp)[p] = dw;
     } else {
-        const int64_t R = p / (Kp / 32), b = p % (Kp / 32);
+        // BLK32: per 32-row group and quad, 16 bytes; byte 4 j + u holds
+        // block 4 (4 q + u) + j
+        const int64_t R = p / (Q * 16), rem = p % (Q * 16);
+        const int64_t q = rem / 16, jj = (rem % 16) / 4, u = rem % 4;
+        const int64_t b = 4 * (4 * q + u) + jj;
         uint32_t c = 128;
         if (b < KB) {
             c = codes[R * KB + b];
@@ -79,6 +84,37 @@ __global__ void __launch_bounds__(256) pack_codes_kernel(
         cp[p] = (uint8_t)c;
     }
     if (found) atomicOr(bad, 1);
+}
+
+// Row-major activation codes [M, ldc] -> XC-T16: per 16-row tile and quad of
+// four 128-K steps, 256 bytes; lane l = 16 j + r's dword holds row r's code
+// of block 4 (4 q + u) + j in byte u (the lane order of the scaled MFMA's
+// B-operand scales).  Rows past M and blocks past K/32 get code 127.
+__global__ void __launch_bounds__(256) act_codes_t16_kernel(int64_t M, int64_t K,
+                                                            const uint8_t *__restrict__ xc,
+                                                            int64_t ldc, uint32_t *__restrict__ out,
+                                                            int64_t ndw) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= ndw) return;
+    const int64_t S = (K + 127) / 128, Q = (S + 3) / 4, KB = K / 32;
+    const int64_t lane = p % 64, mq = p / 64, q = mq % Q, mt = mq / Q;
+    const int64_t row = 16 * mt + lane % 16, j = lane / 16;
+    uint32_t dw = 0;
+    for (int u = 0; u < 4; ++u) {
+        const int64_t b = 4 * (4 * q + u) + j;
+        const uint32_t c = (row < M && b < KB) ? xc[row * ldc + b] : 127u;
+        dw |= c << (8 * u);
+    }
+    out[p] = dw;
+}
+
+hipError_t launch_act_codes_t16(int64_t M, int64_t K, const void *xc, int64_t ldc, void *out,
+                                hipStream_t stream) {
+    const int64_t S = (K + 127) / 128, Q = (S + 3) / 4;
+    const int64_t ndw = (M + 15) / 16 * Q * 64;
+    hipLaunchKernelGGL(act_codes_t16_kernel, dim3((unsigned)((ndw + 255) / 256)), dim3(256), 0,
+                       stream, M, K, (const uint8_t *)xc, ldc, (uint32_t *)out, ndw);
+    return hipGetLastError();
 }
 
 hipError_t launch_pack(int elem, int layout, int64_t E, int64_t N, int64_t K, const void *w,
@@ -90,7 +126,7 @@ hipError_t launch_pack(int elem, int layout, int64_t E, int64_t N, int64_t K, co
                        stream, elem, E, N, K, (const uint8_t *)w, (uint8_t *)wp, npieces);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    const int64_t nunits = layout == ROW32 ? E * (N / 16) * Q * 64 : E * (N / 32) * (Kp / 32);
+    const int64_t nunits = layout == ROW32 ? E * (N / 16) * Q * 64 : E * (N / 32) * Q * 16;
     hipLaunchKernelGGL(pack_codes_kernel, dim3((unsigned)((nunits + 255) / 256)), dim3(256), 0,
                        stream, layout, E, N, K, (const uint8_t *)codes, (uint8_t *)cp, nunits,
                        bad);

@@ -245,7 +245,13 @@ void orc_quant_act(int64_t M, int64_t K, const uint16_t *x, int64_t ldx,
  *
  *   cp[((e T + t) Q + q) 256 + 4 l + u] = codes[e N + 16 t + r][4 (4 q + u) + j]
  *
- * Codes BLK32 ([E N/32, K/32] in) -> row-major [E N/32, Kp/32].
+ * Codes BLK32 ([E N/32, K/32] in) -> [E N/32][Q][16]: for each 32-row group
+ * and quad, 16 bytes; lane group j's dword (bytes 4 j .. 4 j + 3) holds the
+ * group's codes of block 4 s + j for the quad's four steps s = 4 q + u in
+ * byte u -- the same dword-per-lane-group, byte-per-step staging as C-T16.
+ *
+ *   cp[(R Q + q) 16 + 4 j + u] = codes[R][4 (4 q + u) + j]
+ *
  * Every code of a block outside [0, K/32) is 128 (R4).
  */
 
@@ -264,7 +270,7 @@ int orc_packed_sizes(int elem, int layout, int64_t E, int64_t N, int64_t K,
     if (layout == ORC_ROW32)
         *c_bytes = E * (N / 16) * Q * 256;
     else
-        *c_bytes = E * (N / 32) * (Kp / 32);
+        *c_bytes = E * (N / 32) * Q * 16;
     return 0;
 }
 
@@ -308,10 +314,15 @@ int orc_pack_weights(int elem, int layout, int64_t E, int64_t N, int64_t K,
                             cp[dst] = blk < K / 32 ? codes[(e * N + 16 * t + r) * (K / 32) + blk] : 128;
                         }
     } else {
-        int64_t R, b;
+        int64_t R, jj;
         for (R = 0; R < E * N / 32; R++)
-            for (b = 0; b < Kp / 32; b++)
-                cp[R * (Kp / 32) + b] = b < K / 32 ? codes[R * (K / 32) + b] : 128;
+            for (q = 0; q < Q; q++)
+                for (jj = 0; jj < 4; jj++)
+                    for (u = 0; u < 4; u++) {
+                        int64_t blk = 4 * (4 * q + u) + jj;
+                        int64_t dst = (R * Q + q) * 16 + 4 * jj + u;
+                        cp[dst] = blk < K / 32 ? codes[R * (K / 32) + blk] : 128;
+                    }
     }
     return 0;
 }

@@ -41,7 +41,8 @@ def _ref_codes(layout, E, N, K, codes):
     if layout == ROW32:
         v = _pad_cols(codes.reshape(E * N, K // 32), 16 * Q, 128).reshape(E, T, 16, Q, 4, 4)
         return v.transpose(0, 1, 3, 5, 2, 4).reshape(-1)      # [e,t,q,j,r,u]
-    return _pad_cols(codes.reshape(E * N // 32, K // 32), Kp // 32, 128).reshape(-1)
+    v = _pad_cols(codes.reshape(E * N // 32, K // 32), 16 * Q, 128).reshape(-1, Q, 4, 4)
+    return v.transpose(0, 1, 3, 2).reshape(-1)                # [R,q,j,u]
 
 
 SHAPES = [
@@ -148,9 +149,10 @@ def test_padding_bytes_zero_and_codes_128():
     w2 = np.full((1, 64, K), 0x22, np.uint8)
     c2 = np.full((2, K // 32), 9, np.uint8)
     wp2, cp2 = oracle.pack_weights(E4M3, BLK32, 1, 64, K, w2, c2)
-    assert cp2.shape == (2 * Kp // 32,)
-    np.testing.assert_array_equal(cp2.reshape(2, -1)[:, K // 32:], 128)
-    np.testing.assert_array_equal(cp2.reshape(2, -1)[:, : K // 32], 9)
+    assert cp2.shape == (2 * Q * 16,)
+    # 49 real blocks per 32-row group, the other 15 of the 4 quads are padding
+    assert np.count_nonzero(cp2 == 9) == 2 * (K // 32)
+    assert np.count_nonzero(cp2 == 128) == 2 * (16 * Q - K // 32)
 
 
 def test_pack_rejects_bad_shapes():
