@@ -255,7 +255,7 @@ def cpu_baseline(wl):
     N, K = d["N"], d["K"]
     alg = N * K + (N // 32) * (K // 32)
     runs, t_total = 0, 0.0
-    while t_total < 10.0 and runs < 20:
+    while t_total < 12.0 and runs < 2000:
         t = time.perf_counter()
         xq, xc = oracle.quant_act(d["x"], oracle.RULE_OCP)
         oracle.linear(0, 1, N, K, d["w"], d["codes"], 16, oracle.ACT_MXFP8, xq=xq, xcodes=xc)
@@ -327,15 +327,18 @@ def main():
         else:
             s["roofline_frac"] = round(s["kernel_tflops"] / FP8_PEAK_TFLOPS, 4)
 
-    sha = source_sha("mx_gemv.hip", "mx_device.h")
+    for s in [head] + sec:
+        srcs = ("mx_gemv.hip",) if s["unit"] == "GB/s" else ("mx_gemm.hip",)
+        s["traffic"] = recorded_traffic(s["workload"], source_sha(*srcs, "mx_device.h"))
     if head["unit"] == "GB/s":
         roof = {"bound": "hbm", "achieved": round(head["kernel_gbs"], 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(head["kernel_gbs"] / HBM_PEAK_GBS, 4),
-                "traffic": recorded_traffic(head["workload"], sha)}
+                "traffic": head["traffic"]}
     else:
         roof = {"bound": "mfma", "achieved": round(head["kernel_tflops"], 1),
                 "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(head["kernel_tflops"] / FP8_PEAK_TFLOPS, 4), "traffic": None}
+                "frac": round(head["kernel_tflops"] / FP8_PEAK_TFLOPS, 4),
+                "traffic": head["traffic"]}
     cpu = None if args.no_cpu else cpu_baseline(wl)
     out = {
         "metric": "achieved HBM GB/s (weights+scales) for M≤16 MX GEMV; TFLOP/s for M=4096 GEMM",
