@@ -9,11 +9,13 @@
 // v_mfma_scale_f32_16x16x128_f8f6f4 (A = weights, B = activations, both
 // with per-lane E8M0 scales).  Per 128-K step the workgroup copies its
 // weight chunks (W-T16: each 2 KB chunk is already one operand in lane
-// order) and its activation rows (row-major, padded to a 144-byte pitch so
-// the operand reads are bank-conflict free) into one of two LDS buffers
-// while the matrix cores work on the other; one barrier per step.
-// Loads of the next step are issued before the current step's MFMAs.
-// Out-of-range rows and K tails read zeros through buffer-resource bounds.
+// order) and its activation rows (rearranged into the same fragment order
+// by the copy's addressing) straight from memory into one of two LDS
+// buffers (buffer loads with an LDS destination) while the matrix cores
+// work on the other; one barrier per step.  Scale codes are read once per
+// four steps as one dword per lane (byte u = step 4q + u) and the MFMA's
+// byte select picks the step's code.  Out-of-range rows and K tails read
+// zeros through buffer-resource bounds.
 #include "mx_device.h"
 #include "mx_kernels.h"
 
