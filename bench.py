@@ -3,25 +3,28 @@
 
 Headline workload: the W8A8 MXFP8 decode GEMV with 32x32 block scales,
 M = 16 tokens, N = K = 7168.  One step is the whole hot path for one batch:
-per-token MXFP8 quantization of the bf16 activations (OCP rule) followed by
-the GEMV.  Weights and codes are packed once (load time, untimed); the step
-rotates over enough packed copies (>= 512 MiB) that the 256 MB Infinity
-Cache cannot serve them, so every step streams its weights from HBM.
+one mx_linear call on the bf16 activations, which quantizes them per token
+(MXFP8, OCP rule) and runs the GEMV.  Weights and codes are packed once
+(load time, untimed); the step rotates over enough packed copies
+(>= 512 MiB) that the 256 MB Infinity Cache cannot serve them, so every step
+streams its weights from HBM.
 
 value   = algorithmic weight + scale bytes per step / step time  (GB/s)
 roofline.achieved = the same bytes / the GEMV kernel's average duration per
-          launch: `steps` GEMV launches replayed back to back from a HIP graph
-          on the library's stream, timed with HIP events (inter-launch gaps
-          included, so this is a lower bound on the kernel's own rate).
+          launch: `steps` GEMV launches (mx_linear on a pre-quantized T16
+          activation) replayed back to back from a HIP graph on the current
+          stream, timed with HIP events (inter-launch gaps included, so this
+          is a lower bound on the kernel's own rate).
 
 The other workloads are timed the same way and reported under "secondary":
-M = 1 and 4 of the same GEMV, the A16W8 GEMVs (M = 1, N = 256, K = 512 and
-M = 8, N = 4096, K = 1568), the A16W4 grouped MoE GEMV (E = 32, N = K =
-3072, 16 tokens top-8) and the prefill W8A8 GEMM (M = 4096, N = K = 7168,
-quantization + GEMM per step; TFLOP/s against the 5.0 PFLOP/s fp8 peak).
+M = 1 and 4 of the same GEMV, the same GEMV fed by mx_quant_act's row-major
+output, the A16W8 GEMVs (M = 1, N = 256, K = 512 and M = 8, N = 4096,
+K = 1568), the A16W4 grouped MoE GEMV (E = 32, N = K = 3072, 16 tokens
+top-8) and the prefill W8A8 GEMM (M = 4096, N = K = 7168, quantization +
+GEMM per step; TFLOP/s against the 5.0 PFLOP/s fp8 peak).
 
 cpu_baseline: the CPU oracle (fp64, OpenMP) computing the headline step on
-the host cores, timed on the full workload, repeated for about 10 s.
+the host cores, timed on the full workload, repeated for about 12 s.
 """
 from __future__ import annotations
 
@@ -49,7 +52,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None,
-                    help="run one workload only (gemv16, gemv1, gemv4, a16_c1, a16_c3, moe, gemm)")
+                    help="run one workload only (gemv16, gemv1, gemv4, gemv16r, a16_c1, a16_c3, "
+                         "moe, gemm)")
     ap.add_argument("--eager", action="store_true",
                     help="launch without HIP graphs (for hardware-counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -150,29 +154,60 @@ def setup_dense(torch, mx, g, wl, cid, M, rotate=True):
     return d, wps, cps
 
 
-def bench_w8a8_gemv(torch, mx, g, wl, M, steps, warmup):
+def bench_w8a8_gemv(torch, mx, g, wl, M, steps, warmup, rowmajor=False):
+    """W8A8 decode GEMV, N = K = 7168, 32x32 block codes.
+
+    Default: one mx_linear call per step with the activation quantized inside
+    the call (per token, OCP rule, into the T16 layout), then the GEMV; the
+    kernel-only timing runs the same GEMV on a pre-quantized T16 activation.
+    rowmajor: mx_quant_act (row-major output) then mx_linear on it."""
     d, wps, cps = setup_dense(torch, mx, g, wl, 2, M)
     N, K = d["N"], d["K"]
     x = g.dev(d["x"][:M])
-    xq = torch.empty((M, K), dtype=torch.uint8, device=g.DEV)
-    xc = torch.empty((M, K // 32), dtype=torch.uint8, device=g.DEV)
     y = torch.empty((M, N), dtype=torch.int16, device=g.DEV)
     nc = len(wps)
+    E, L, A8, T16 = mx.MX_E4M3, mx.MX_SCALE_BLK32, mx.MX_ACT_MXFP8, mx.MX_ACT_MXFP8_T16
+    if rowmajor:
+        xq = torch.empty((M, K), dtype=torch.uint8, device=g.DEV)
+        xc = torch.empty((M, K // 32), dtype=torch.uint8, device=g.DEV)
 
-    def step(i):
-        mx.mx_quant_act(M, K, x, K, xq, K, xc, K // 32, mx.MX_RULE_OCP)
+        def step(i):
+            mx.mx_quant_act(M, K, x, K, xq, K, xc, K // 32, mx.MX_RULE_OCP)
 
-    def kernel(i):
-        mx.mx_linear(mx.MX_E4M3, mx.MX_SCALE_BLK32, N, K, wps[i % nc], cps[i % nc], M,
-                     mx.MX_ACT_MXFP8, mx.MX_RULE_OCP, None, 0, xq, K, xc, K // 32, None, y, N,
-                     None, 0)
+        def kernel(i):
+            mx.mx_linear(E, L, N, K, wps[i % nc], cps[i % nc], M, A8, mx.MX_RULE_OCP, None, 0,
+                         xq, K, xc, K // 32, None, y, N, None, 0)
 
-    ms_step, ms_k = GraphTimer(torch).run(step, kernel, steps, warmup)
+        ms_step, ms_k = GraphTimer(torch).run(step, kernel, steps, warmup)
+        how = "mx_quant_act (row-major) + mx_linear on it"
+        kname = "gemv_w8_kernel (BLK32, row-major activations)"
+    else:
+        need = mx.mx_linear_workspace(E, L, N, K, M, A8, 0)
+        ws = torch.empty(need, dtype=torch.uint8, device=g.DEV)
+        qb, cb = mx.mx_act_t16_sizes(M, K)
+        xq = torch.empty(qb, dtype=torch.uint8, device=g.DEV)
+        xc = torch.empty(cb, dtype=torch.uint8, device=g.DEV)
+        mx.mx_quant_act_t16(M, K, x, K, xq, xc, mx.MX_RULE_OCP)
+
+        def step(i):
+            mx.mx_linear(E, L, N, K, wps[i % nc], cps[i % nc], M, A8, mx.MX_RULE_OCP, x, K,
+                         None, 0, None, 0, None, y, N, ws, need)
+
+        def kernel(i):
+            mx.mx_linear(E, L, N, K, wps[i % nc], cps[i % nc], M, T16, mx.MX_RULE_OCP, None, 0,
+                         xq, 0, xc, 0, None, y, N, None, 0)
+
+        timer = GraphTimer(torch)
+        ms_step = timer.time(step, steps, warmup)
+        ms_k = timer.time(kernel, steps, warmup)
+        how = "mx_linear with in-call MXFP8 quantization (OCP rule)"
+        kname = "gemv_w8_kernel (BLK32, T16 activations)"
     alg = N * K + (N // 32) * (K // 32)
-    return dict(workload=f"mxfp8_w8a8_gemv_M{M}_N{N}_K{K}_blk32", M=M, N=N, K=K,
-                bytes_per_step=alg, weight_copies=nc, ms_per_step=ms_step, ms_kernel=ms_k,
-                value=alg / (ms_step * 1e-3) / 1e9, unit="GB/s",
-                kernel_gbs=alg / (ms_k * 1e-3) / 1e9, kernel="gemv_kernel (W8A8, BLK32)")
+    return dict(workload=f"mxfp8_w8a8_gemv_M{M}_N{N}_K{K}_blk32" + ("_rowmajor" if rowmajor else ""),
+                M=M, N=N, K=K, bytes_per_step=alg, weight_copies=nc, ms_per_step=ms_step,
+                ms_kernel=ms_k, value=alg / (ms_step * 1e-3) / 1e9, unit="GB/s",
+                kernel_gbs=alg / (ms_k * 1e-3) / 1e9, kernel=kname, step=how,
+                src="mx_gemv_w8.hip")
 
 
 def bench_a16_gemv(torch, mx, g, wl, cid, steps, warmup):
@@ -192,7 +227,8 @@ def bench_a16_gemv(torch, mx, g, wl, cid, steps, warmup):
     return dict(workload=wl.CONFIGS[cid]["name"], M=M, N=N, K=K, bytes_per_step=alg,
                 weight_copies=nc, ms_per_step=ms_step, ms_kernel=ms_k,
                 value=alg / (ms_step * 1e-3) / 1e9, unit="GB/s",
-                kernel_gbs=alg / (ms_k * 1e-3) / 1e9, kernel="gemv_kernel (A16W8, ROW32)")
+                kernel_gbs=alg / (ms_k * 1e-3) / 1e9, kernel="gemv_kernel (A16W8, ROW32)",
+                src="mx_gemv.hip")
 
 
 def bench_moe(torch, mx, g, wl, steps, warmup):
@@ -220,33 +256,42 @@ def bench_moe(torch, mx, g, wl, steps, warmup):
                 experts_touched=touched, bytes_per_step=alg, weight_copies=nc,
                 ms_per_step=ms_step, ms_kernel=ms_k, value=alg / (ms_step * 1e-3) / 1e9,
                 unit="GB/s", kernel_gbs=alg / (ms_k * 1e-3) / 1e9,
-                kernel="gemv_kernel (A16W4, MoE)")
+                kernel="gemv_kernel (A16W4, MoE)", src="mx_gemv.hip")
 
 
 def bench_gemm(torch, mx, g, wl, steps, warmup):
+    """Prefill W8A8 GEMM, M = 4096, N = K = 7168: per step one mx_linear with
+    the activation quantized inside the call (T16 layout) then the GEMM; the
+    kernel-only timing runs the GEMM on a pre-quantized T16 activation."""
     d = wl.linear_inputs(5)
     N, K, M = d["N"], d["K"], d["M"]
     wp, cp = g.pack(0, 1, 1, N, K, d["w"], d["codes"])
     x = g.dev(d["x"])
-    xq = torch.empty((M, K), dtype=torch.uint8, device=g.DEV)
-    xc = torch.empty((M, K // 32), dtype=torch.uint8, device=g.DEV)
     y = torch.empty((M, N), dtype=torch.int16, device=g.DEV)
-    need = mx.mx_linear_workspace(0, 1, N, K, M, mx.MX_ACT_MXFP8, 1)
-    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=g.DEV)
+    need = mx.mx_linear_workspace(0, 1, N, K, M, mx.MX_ACT_MXFP8, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device=g.DEV)
+    qb, cb = mx.mx_act_t16_sizes(M, K)
+    xq = torch.empty(qb, dtype=torch.uint8, device=g.DEV)
+    xc = torch.empty(cb, dtype=torch.uint8, device=g.DEV)
+    mx.mx_quant_act_t16(M, K, x, K, xq, xc, mx.MX_RULE_OCP)
 
     def step(i):
-        mx.mx_quant_act(M, K, x, K, xq, K, xc, K // 32, mx.MX_RULE_OCP)
+        mx.mx_linear(0, 1, N, K, wp, cp, M, mx.MX_ACT_MXFP8, mx.MX_RULE_OCP, x, K, None, 0,
+                     None, 0, None, y, N, ws, need)
 
     def kernel(i):
-        mx.mx_linear(0, 1, N, K, wp, cp, M, mx.MX_ACT_MXFP8, 0, None, 0, xq, K, xc, K // 32,
-                     None, y, N, ws, need)
+        mx.mx_linear(0, 1, N, K, wp, cp, M, mx.MX_ACT_MXFP8_T16, 0, None, 0, xq, 0, xc, 0,
+                     None, y, N, None, 0)
 
-    ms_step, ms_k = GraphTimer(torch).run(step, kernel, steps, warmup)
+    timer = GraphTimer(torch)
+    ms_step = timer.time(step, steps, warmup)
+    ms_k = timer.time(kernel, steps, warmup)
     flop = 2.0 * M * N * K
     return dict(workload=wl.CONFIGS[5]["name"], M=M, N=N, K=K, flop_per_step=flop,
                 ms_per_step=ms_step, ms_kernel=ms_k, value=flop / (ms_step * 1e-3) / 1e12,
                 unit="TFLOP/s", kernel_tflops=flop / (ms_k * 1e-3) / 1e12,
-                kernel="gemm_w8a8_kernel (BLK32)")
+                kernel="gemm_w8a8_kernel (BLK32, T16 activations)",
+                step="mx_linear with in-call MXFP8 quantization (OCP rule)", src="mx_gemm.hip")
 
 
 def cpu_baseline(wl):
@@ -308,6 +353,9 @@ def main():
     if not args.no_secondary:
         if want("gemv1"):
             sec.append(bench_w8a8_gemv(torch, mx, g, wl, 1, K, W)); log(json.dumps(sec[-1]))
+        if want("gemv16r"):
+            sec.append(bench_w8a8_gemv(torch, mx, g, wl, 16, K, W, rowmajor=True))
+            log(json.dumps(sec[-1]))
         if want("gemv4"):
             sec.append(bench_w8a8_gemv(torch, mx, g, wl, 4, K, W)); log(json.dumps(sec[-1]))
         if want("a16_c1"):
@@ -328,8 +376,7 @@ def main():
             s["roofline_frac"] = round(s["kernel_tflops"] / FP8_PEAK_TFLOPS, 4)
 
     for s in [head] + sec:
-        srcs = ("mx_gemv.hip",) if s["unit"] == "GB/s" else ("mx_gemm.hip",)
-        s["traffic"] = recorded_traffic(s["workload"], source_sha(*srcs, "mx_device.h"))
+        s["traffic"] = recorded_traffic(s["workload"], source_sha(s["src"], "mx_device.h"))
     if head["unit"] == "GB/s":
         roof = {"bound": "hbm", "achieved": round(head["kernel_gbs"], 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(head["kernel_gbs"] / HBM_PEAK_GBS, 4),
@@ -354,7 +401,7 @@ def main():
         "dtype": "mxfp8",
         "data": "synthetic",
         "config": {"workload": head["workload"], "M": head.get("M"), "N": head.get("N"),
-                   "K": head.get("K"), "step": "per-token MXFP8 quant (OCP rule) + GEMV",
+                   "K": head.get("K"), "step": head.get("step"),
                    "weight_copies_rotated": head.get("weight_copies"),
                    "gemv_kernel_ms": round(head["ms_kernel"], 5)},
         "roofline": roof,

@@ -67,8 +67,24 @@ typedef enum { MX_RULE_OCP = 0, MX_RULE_CEIL448 = 1 } mx_quant_rule;
 /* MX_ACT_BF16: activations stay bf16 (A16W8 / A16W4).
  * MX_ACT_MXFP8: activations are MXFP8, e4m3 bytes [M, K] with row-major
  * E8M0 codes [M, K/32] ([rocm_native] input_quant_key: row-major, not
- * swizzled), either given pre-quantized or quantized inside the call (W8A8). */
-typedef enum { MX_ACT_BF16 = 0, MX_ACT_MXFP8 = 1 } mx_act;
+ * swizzled), either given pre-quantized or quantized inside the call (W8A8).
+ * MX_ACT_MXFP8_T16: MXFP8 activations pre-quantized by mx_quant_act_t16 into
+ * the library's 16-token tile layout (below); the same values as
+ * MX_ACT_MXFP8, stored the way the matrix cores read them, so a quantized
+ * activation can be shared by several linears without re-reading it
+ * row-major. */
+typedef enum { MX_ACT_BF16 = 0, MX_ACT_MXFP8 = 1, MX_ACT_MXFP8_T16 = 2 } mx_act;
+
+/*
+ * T16 activation layout (this library's own; the values are those of
+ * mx_quant_act).  S = ceil(K / 128) steps, Q = ceil(S / 4), MB = ceil(M / 16)
+ * token tiles, lane l = 16 j + r:
+ *   xq     MB * S * 2048 bytes: byte ((mb S + s) 2 + h) 1024 + 16 l + c is
+ *          the e4m3 value of token 16 mb + r at K 128 s + 64 h + 16 j + c;
+ *   xcodes MB * Q * 256 bytes: byte (mb Q + q) 256 + 4 l + u is the code of
+ *          token 16 mb + r, block 4 (4 q + u) + j.
+ * Tokens past M and K past the end hold byte 0 and code 127.
+ */
 
 /*
  * Packed weight layout ("W-T16", [weights942] dense_copy / fp4_tile_major
@@ -121,12 +137,24 @@ mx_status mx_quant_act(int64_t M, int64_t K, const void *x, int64_t ldx,
                        void *xq, int64_t ldq, void *xcodes, int64_t ldc,
                        int rule, mx_stream_t stream);
 
-/* Workspace bytes mx_linear needs for these arguments (0 when none), for
- * act == MX_ACT_MXFP8:
- *   M * Kp + M * Kp / 32 (each rounded up to 256) when the activation is
- *   quantized inside the call (prequantized = 0), plus
- *   ceil(M / 16) * Q * 256 when M > 64 (the prefill GEMM path restages the
- *   row-major activation codes into 16-row tiles, pre-quantized or not). */
+/* Sizes (host) of the T16 quantized activation of M tokens x K.
+ * Rules: M >= 1, K >= 32, K % 32 == 0. */
+mx_status mx_act_t16_sizes(int64_t M, int64_t K, size_t *xq_bytes, size_t *xcodes_bytes);
+
+/* Per-token MXFP8 quantization into the T16 layout: the same bytes and codes
+ * as mx_quant_act, rearranged ([rocm_native] _quant_mxfp8_tile).
+ *   x      (device) bf16 [M, ldx], 16-byte aligned, ldx % 8 == 0, ldx >= K
+ *   xq, xcodes (device) outputs of mx_act_t16_sizes' sizes, 16-byte aligned
+ * Every byte of both outputs is written. */
+mx_status mx_quant_act_t16(int64_t M, int64_t K, const void *x, int64_t ldx, void *xq,
+                           void *xcodes, int rule, mx_stream_t stream);
+
+/* Workspace bytes mx_linear needs for these arguments (0 when none):
+ *   act == MX_ACT_MXFP8 quantized inside the call (prequantized = 0): the
+ *     T16 activation, round256(MB * S * 2048) + MB * Q * 256;
+ *   act == MX_ACT_MXFP8 pre-quantized row-major with M > 64 (prefill GEMM):
+ *     MB * Q * 256 for the codes restaged into the T16 code layout;
+ *   otherwise 0 (MX_ACT_BF16, MX_ACT_MXFP8_T16, or pre-quantized M <= 64). */
 mx_status mx_linear_workspace(int elem, int layout, int64_t N, int64_t K,
                               int64_t M, int act, int prequantized,
                               size_t *bytes);
@@ -137,7 +165,9 @@ mx_status mx_linear_workspace(int elem, int layout, int64_t N, int64_t K,
  *   a = x (bf16) when act == MX_ACT_BF16;
  *   a = dec(xq) * 2^(xcode - 127) when act == MX_ACT_MXFP8: if xq and xcodes
  *       are both non-NULL they are used as given (pre-quantized, row-major
- *       codes); otherwise x is quantized first with `rule` into ws.
+ *       codes); otherwise x is quantized first with `rule` into ws;
+ *   the same with xq, xcodes in the T16 layout when act == MX_ACT_MXFP8_T16
+ *       (ldq, ldc, x and rule unused).
  *   w_packed, codes_packed (device) from mx_pack_weights with the same
  *       elem, layout, E = 1, N, K.
  *   x   (device) bf16 [M, ldx]: 16-byte aligned, ldx % 8 == 0, ldx >= K
@@ -149,7 +179,7 @@ mx_status mx_linear_workspace(int elem, int layout, int64_t N, int64_t K,
  *       (may be NULL when that is 0); its contents on return are unspecified
  * The call is asynchronous on `stream`, allocates nothing and may be
  * captured in a graph.
- * Built combinations: E4M3 x {ROW32, BLK32} x {BF16, MXFP8};
+ * Built combinations: E4M3 x {ROW32, BLK32} x {BF16, MXFP8, MXFP8_T16};
  * E2M1 x ROW32 x BF16.  Others: MX_ERR_UNSUPPORTED. */
 mx_status mx_linear(int elem, int layout, int64_t N, int64_t K,
                     const void *w_packed, const void *codes_packed, int64_t M,

@@ -19,8 +19,9 @@ import os
 
 __all__ = [
     "MX_E4M3", "MX_E2M1", "MX_SCALE_ROW32", "MX_SCALE_BLK32", "MX_RULE_OCP",
-    "MX_RULE_CEIL448", "MX_ACT_BF16", "MX_ACT_MXFP8", "MXError", "lib",
-    "mx_packed_sizes", "mx_pack_weights", "mx_quant_act", "mx_linear_workspace",
+    "MX_RULE_CEIL448", "MX_ACT_BF16", "MX_ACT_MXFP8", "MX_ACT_MXFP8_T16", "MXError", "lib",
+    "mx_packed_sizes", "mx_pack_weights", "mx_quant_act", "mx_act_t16_sizes",
+    "mx_quant_act_t16", "mx_linear_workspace",
     "mx_linear", "mx_moe_workspace", "mx_moe_linear", "mx_status_str",
     "mx_arch_supported",
 ]
@@ -28,7 +29,7 @@ __all__ = [
 MX_E4M3, MX_E2M1 = 0, 1
 MX_SCALE_ROW32, MX_SCALE_BLK32 = 0, 1
 MX_RULE_OCP, MX_RULE_CEIL448 = 0, 1
-MX_ACT_BF16, MX_ACT_MXFP8 = 0, 1
+MX_ACT_BF16, MX_ACT_MXFP8, MX_ACT_MXFP8_T16 = 0, 1, 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmx.so")
 _lib = None
@@ -57,14 +58,17 @@ def lib() -> C.CDLL:
         L.mx_packed_sizes.argtypes = [i32, i32, i64, i64, i64, C.POINTER(sz), C.POINTER(sz)]
         L.mx_pack_weights.argtypes = [i32, i32, i64, i64, i64, p, p, p, p, p, sz, p]
         L.mx_quant_act.argtypes = [i64, i64, p, i64, p, i64, p, i64, i32, p]
+        L.mx_act_t16_sizes.argtypes = [i64, i64, C.POINTER(sz), C.POINTER(sz)]
+        L.mx_quant_act_t16.argtypes = [i64, i64, p, i64, p, p, i32, p]
         L.mx_linear_workspace.argtypes = [i32, i32, i64, i64, i64, i32, i32, C.POINTER(sz)]
         L.mx_linear.argtypes = [i32, i32, i64, i64, p, p, i64, i32, i32, p, i64, p, i64,
                                 p, i64, p, p, i64, p, sz, p]
         L.mx_moe_workspace.argtypes = [i32, i64, i64, i64, i64, i64, i32, C.POINTER(sz)]
         L.mx_moe_linear.argtypes = [i32, i64, i64, i64, p, p, i64, i64, p, i64, p, p, p,
                                     p, sz, p]
-        for name in ("mx_packed_sizes", "mx_pack_weights", "mx_quant_act", "mx_linear_workspace",
-                     "mx_linear", "mx_moe_workspace", "mx_moe_linear"):
+        for name in ("mx_packed_sizes", "mx_pack_weights", "mx_quant_act", "mx_act_t16_sizes",
+                     "mx_quant_act_t16", "mx_linear_workspace", "mx_linear", "mx_moe_workspace",
+                     "mx_moe_linear"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -117,6 +121,17 @@ def mx_pack_weights(elem, layout, E, N, K, w, codes, w_packed, codes_packed, ws,
 def mx_quant_act(M, K, x, ldx, xq, ldq, xcodes, ldc, rule, stream=None):
     _check(lib().mx_quant_act(M, K, _ptr(x), ldx, _ptr(xq), ldq, _ptr(xcodes), ldc, rule,
                               _stream(stream)), "mx_quant_act")
+
+
+def mx_act_t16_sizes(M, K):
+    qb, cb = C.c_size_t(), C.c_size_t()
+    _check(lib().mx_act_t16_sizes(M, K, C.byref(qb), C.byref(cb)), "mx_act_t16_sizes")
+    return qb.value, cb.value
+
+
+def mx_quant_act_t16(M, K, x, ldx, xq, xcodes, rule, stream=None):
+    _check(lib().mx_quant_act_t16(M, K, _ptr(x), ldx, _ptr(xq), _ptr(xcodes), rule,
+                                  _stream(stream)), "mx_quant_act_t16")
 
 
 def mx_linear_workspace(elem, layout, N, K, M, act, prequantized):

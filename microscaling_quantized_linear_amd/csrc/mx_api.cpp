@@ -16,6 +16,7 @@ namespace {
 
 using mx::ACT_BF16;
 using mx::ACT_MXFP8;
+using mx::ACT_MXFP8_T16;
 using mx::BLK32;
 using mx::E2M1;
 using mx::E4M3;
@@ -27,6 +28,12 @@ constexpr int64_t kMaxRsrc = (int64_t(1) << 31) - 1;   // 32-bit buffer offsets
 constexpr int64_t kGemvMaxM = 64;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
+
+// the W8A8 GEMV's launch plan (fails for more than 64 steps of K per wavefront)
+mx::GemvW8Plan gemv_w8_plan(int64_t N, int64_t K, int64_t M) {
+    return mx::plan_gemv_w8(N / 16, (K + 127) / 128, (M + 15) / 16);
+}
 int64_t padded_k(int64_t K) { return (K + 127) / 128 * 128; }
 
 mx_status shape_ok(int elem, int layout, int64_t E, int64_t N, int64_t K) {
@@ -160,21 +167,43 @@ mx_status mx_quant_act(int64_t M, int64_t K, const void *x, int64_t ldx, void *x
                                      reinterpret_cast<hipStream_t>(stream)));
 }
 
+mx_status mx_act_t16_sizes(int64_t M, int64_t K, size_t *xq_bytes, size_t *xcodes_bytes) {
+    if (!xq_bytes || !xcodes_bytes) return MX_ERR_NULL;
+    if (M < 1 || K < 32 || K % 32 != 0) return MX_ERR_SHAPE;
+    *xq_bytes = (size_t)mx::act_t16_data_bytes(M, K);
+    *xcodes_bytes = (size_t)mx::act_codes_t16_bytes(M, K);
+    return MX_OK;
+}
+
+mx_status mx_quant_act_t16(int64_t M, int64_t K, const void *x, int64_t ldx, void *xq,
+                           void *xcodes, int rule, mx_stream_t stream) {
+    if (rule != mx::RULE_OCP && rule != mx::RULE_CEIL448) return MX_ERR_UNSUPPORTED;
+    if (M < 1 || K < 32 || K % 32 != 0 || ldx < K) return MX_ERR_SHAPE;
+    if (!x || !xq || !xcodes) return MX_ERR_NULL;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(xcodes) || ldx % 8 != 0)
+        return MX_ERR_ALIGN;
+    if (mx::act_t16_data_bytes(M, K) > kMaxRsrc) return MX_ERR_SHAPE;
+    mx_status st = device_ok();
+    if (st != MX_OK) return st;
+    return launched(mx::launch_quant_t16(M, K, x, ldx, xq, xcodes, rule,
+                                         reinterpret_cast<hipStream_t>(stream)));
+}
+
 mx_status mx_linear_workspace(int elem, int layout, int64_t N, int64_t K, int64_t M, int act,
                               int prequantized, size_t *bytes) {
     if (!bytes) return MX_ERR_NULL;
     mx_status st = shape_ok(elem, layout, 1, N, K);
     if (st != MX_OK) return st;
     if (M < 1) return MX_ERR_SHAPE;
-    if (act != ACT_BF16 && act != ACT_MXFP8) return MX_ERR_UNSUPPORTED;
+    if (act != ACT_BF16 && act != ACT_MXFP8 && act != ACT_MXFP8_T16) return MX_ERR_UNSUPPORTED;
     *bytes = 0;
-    if (act == ACT_MXFP8) {
-        const int64_t Kp = padded_k(K);
-        int64_t b = 0;
-        if (!prequantized) b += (M * Kp + 255) / 256 * 256 + (M * (Kp / 32) + 255) / 256 * 256;
-        if (M > kGemvMaxM) b += mx::act_codes_t16_bytes(M, K);   // GEMM code staging
-        *bytes = (size_t)b;
-    }
+    const bool long_k = M <= kGemvMaxM && !gemv_w8_plan(N, K, M).ok;
+    if (act == ACT_MXFP8 && !prequantized && !long_k)   // in-call quantization into T16
+        *bytes = (size_t)(round256(mx::act_t16_data_bytes(M, K)) + mx::act_codes_t16_bytes(M, K));
+    else if (act == ACT_MXFP8 && !prequantized)         // row-major, chunked GEMV for long K
+        *bytes = (size_t)(round256(M * padded_k(K)) + round256(M * (padded_k(K) / 32)));
+    else if (act == ACT_MXFP8 && M > kGemvMaxM)         // row-major codes restaged for the GEMM
+        *bytes = (size_t)mx::act_codes_t16_bytes(M, K);
     return MX_OK;
 }
 
@@ -185,7 +214,7 @@ mx_status mx_linear(int elem, int layout, int64_t N, int64_t K, const void *w_pa
                     mx_stream_t stream) {
     mx_status st = shape_ok(elem, layout, 1, N, K);
     if (st != MX_OK) return st;
-    if (act != ACT_BF16 && act != ACT_MXFP8) return MX_ERR_UNSUPPORTED;
+    if (act != ACT_BF16 && act != ACT_MXFP8 && act != ACT_MXFP8_T16) return MX_ERR_UNSUPPORTED;
     if (rule != mx::RULE_OCP && rule != mx::RULE_CEIL448) return MX_ERR_UNSUPPORTED;
     if (elem == E2M1 && (layout != ROW32 || act != ACT_BF16)) return MX_ERR_UNSUPPORTED;
     if (M < 1 || ldy < N) return MX_ERR_SHAPE;
@@ -194,8 +223,10 @@ mx_status mx_linear(int elem, int layout, int64_t N, int64_t K, const void *w_pa
         return MX_ERR_ALIGN;
     if (bias && (reinterpret_cast<uintptr_t>(bias) & 1u)) return MX_ERR_ALIGN;
     const int64_t Kp = padded_k(K);
+    const bool t16 = act == ACT_MXFP8_T16;
     const bool preq = act == ACT_MXFP8 && xq && xcodes;
-    if (act == ACT_BF16 || !preq) {
+    const bool incall = act == ACT_MXFP8 && !preq;
+    if (act == ACT_BF16 || incall) {
         if (!x) return MX_ERR_NULL;
         if (ldx < K) return MX_ERR_SHAPE;
         if (!aligned16(x) || ldx % 8 != 0) return MX_ERR_ALIGN;
@@ -206,34 +237,45 @@ mx_status mx_linear(int elem, int layout, int64_t N, int64_t K, const void *w_pa
         if (!aligned16(xq) || ldq % 16 != 0) return MX_ERR_ALIGN;
         if (M * ldq > kMaxRsrc || M * ldc > kMaxRsrc) return MX_ERR_SHAPE;
     }
+    if (t16) {
+        if (!xq || !xcodes) return MX_ERR_NULL;
+        if (!aligned16(xq) || !aligned16(xcodes)) return MX_ERR_ALIGN;
+    }
+    if ((incall || t16) && mx::act_t16_data_bytes(M, K) > kMaxRsrc) return MX_ERR_SHAPE;
     size_t need = 0;
-    mx_linear_workspace(elem, layout, N, K, M, act, preq ? 1 : 0, &need);
+    mx_linear_workspace(elem, layout, N, K, M, act, incall ? 0 : 1, &need);
     if (need > 0 && (!ws || ws_bytes < need)) return MX_ERR_WORKSPACE;
     if (need > 0 && !aligned16(ws)) return MX_ERR_ALIGN;
-    const bool gemm = act == ACT_MXFP8 && M > kGemvMaxM;
+    const bool gemm = act != ACT_BF16 && M > kGemvMaxM;
     if (gemm && N * Kp > kMaxRsrc) return MX_ERR_SHAPE;
     if ((st = device_ok()) != MX_OK) return st;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    uint8_t *wsp = static_cast<uint8_t *>(ws);
 
+    // the MXFP8 activation: T16 (given, or quantized here into ws) or row-major
     const uint8_t *aq = static_cast<const uint8_t *>(xq);
     const uint8_t *ac = static_cast<const uint8_t *>(xcodes);
     int64_t lq = ldq, lc = ldc;
-    uint8_t *wsp = static_cast<uint8_t *>(ws);
-    if (act == ACT_MXFP8 && !preq) {
-        // quantize into the workspace: e4m3 [M, Kp] then codes [M, Kp/32]
-        uint8_t *q = wsp;
-        uint8_t *c = q + (M * Kp + 255) / 256 * 256;
-        wsp = c + (M * (Kp / 32) + 255) / 256 * 256;
+    bool a16 = t16;
+    const mx::GemvW8Plan w8 = gemv_w8_plan(N, K, M);
+    if (incall && !gemm && !w8.ok) {
+        // K beyond the T16 GEMV's registers: row-major quantization into ws
+        // for the chunked GEMV
+        uint8_t *q = wsp, *c = wsp + round256(M * Kp);
         lq = Kp;
         lc = Kp / 32;
         if ((st = launched(mx::launch_quant(M, K, x, ldx, q, lq, c, lc, rule, s))) != MX_OK)
             return st;
         aq = q;
         ac = c;
+    } else if (incall) {
+        uint8_t *q = wsp, *c = wsp + round256(mx::act_t16_data_bytes(M, K));
+        if ((st = launched(mx::launch_quant_t16(M, K, x, ldx, q, c, rule, s))) != MX_OK) return st;
+        aq = q;
+        ac = c;
+        a16 = true;
     }
     if (gemm) {
-        // restage the activation codes for the GEMM's per-lane scale loads
-        if ((st = launched(mx::launch_act_codes_t16(M, K, ac, lc, wsp, s))) != MX_OK) return st;
         mx::GemmArgs g{};
         g.w = static_cast<const uint8_t *>(w_packed);
         g.codes = static_cast<const uint8_t *>(codes_packed);
@@ -242,12 +284,41 @@ mx_status mx_linear(int elem, int layout, int64_t N, int64_t K, const void *w_pa
         g.M = M;
         g.xq = aq;
         g.ldq = lq;
-        g.xct = wsp;
+        g.xt16 = a16;
+        g.xct = ac;
+        if (!a16) {
+            // restage the row-major codes into the T16 code layout
+            if ((st = launched(mx::launch_act_codes_t16(M, K, ac, lc, wsp, s))) != MX_OK)
+                return st;
+            g.xct = wsp;
+        }
         g.bias = static_cast<const uint16_t *>(bias);
         g.y = static_cast<uint16_t *>(y);
         g.ldy = ldy;
         return launched(mx::launch_gemm(layout, g, s));
     }
+    if (act != ACT_BF16 && w8.ok) {
+        mx::GemvW8Args g{};
+        g.w = static_cast<const uint8_t *>(w_packed);
+        g.codes = static_cast<const uint8_t *>(codes_packed);
+        g.N = N;
+        g.K = K;
+        g.M = M;
+        g.bias = static_cast<const uint16_t *>(bias);
+        g.y = static_cast<uint16_t *>(y);
+        g.ldy = ldy;
+        if (a16) {
+            g.xf = aq;
+            g.xct = ac;
+        } else {
+            g.xq = aq;
+            g.ldq = lq;
+            g.xc = ac;
+            g.ldc = lc;
+        }
+        return launched(mx::launch_gemv_w8(layout, a16, g, w8, s));
+    }
+    if (a16) return MX_ERR_UNSUPPORTED;             // T16 input with K beyond the GEMV plan
     mx::GemvArgs a{};
     a.w = static_cast<const uint8_t *>(w_packed);
     a.codes = static_cast<const uint8_t *>(codes_packed);
@@ -315,13 +386,13 @@ mx_status mx_moe_linear(int elem, int64_t E, int64_t N, int64_t K, const void *w
     a.ids = topk_ids;
     a.y = static_cast<uint16_t *>(y);
     a.ldy = N;
-    a.ws = topk_weights ? static_cast<float *>(ws) : nullptr;
+    float *slots = topk_weights ? static_cast<float *>(ws) : nullptr;
+    a.ws = slots;
     if ((st = launched(mx::launch_gemv(elem, ROW32, ACT_BF16, true, a,
                                        gemv_shape(Kp / 128, true), s))) != MX_OK)
         return st;
     if (topk_weights)
-        return launched(mx::launch_moe_combine(T, topk, N, static_cast<const float *>(ws),
-                                               topk_weights, y, s));
+        return launched(mx::launch_moe_combine(T, topk, N, slots, topk_weights, y, s));
     return MX_OK;
 }
 

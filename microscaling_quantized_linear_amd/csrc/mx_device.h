@@ -29,6 +29,13 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef short v2s __attribute__((ext_vector_type(2)));
 
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// are outstanding and leaves the export and LDS/scalar counters alone
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+__host__ __device__ constexpr int vmcnt_only(int n) {
+    return (n & 0xF) | (0x7 << 4) | (0xF << 8) | (((n >> 4) & 0x3) << 14);
+}
+
 // Cache-policy bits of buffer instructions on gfx950: nt (streamed once).
 constexpr int kNT = 2;
 

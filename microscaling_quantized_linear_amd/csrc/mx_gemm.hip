@@ -9,8 +9,9 @@
 // v_mfma_scale_f32_16x16x128_f8f6f4 (A = weights, B = activations, both
 // with per-lane E8M0 scales).  Per 128-K step the workgroup copies its
 // weight chunks (W-T16: each 2 KB chunk is already one operand in lane
-// order) and its activation rows (rearranged into the same fragment order
-// by the copy's addressing) straight from memory into one of two LDS
+// order) and its activation rows (already in fragment order when they come
+// in the T16 layout, else rearranged into it by the copy's addressing)
+// straight from memory into one of two LDS
 // buffers (buffer loads with an LDS destination) while the matrix cores
 // work on the other; one barrier per step.  Scale codes are read once per
 // four steps as one dword per lane (byte u = step 4q + u) and the MFMA's
@@ -69,7 +70,9 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     const int64_t t0 = n0 / 16;                           // first weight tile
 
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w, (uint32_t)(T * S * 2048));
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.xq, (uint32_t)(p.M * p.ldq));
+    const int64_t MB = (p.M + 15) / 16;
+    const __amdgpu_buffer_rsrc_t xr =
+        make_rsrc(p.xq, p.xt16 ? (uint32_t)(MB * S * 2048) : (uint32_t)(p.M * p.ldq));
     const __amdgpu_buffer_rsrc_t xcr = make_rsrc(p.xct, (uint32_t)act_codes_t16_bytes(p.M, p.K));
     const __amdgpu_buffer_rsrc_t cr =
         make_rsrc(p.codes, LAYOUT == ROW32 ? (uint32_t)(T * Q * 256)
@@ -92,9 +95,18 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     for (int q = 0; q < kXq; ++q) {
         const int i = wave + 4 * q, mc = i / 2, h = i % 2;
         const int64_t row = m0 + 16 * mc + r, k = 64 * h + 16 * j;
-        xbase[q] = row < p.M ? (uint32_t)(row * p.ldq + k) : kOOB;
-        xkmax[q] = (uint32_t)((p.K - k + 127) / 128);     // steps with 128 s + k < K
+        if (p.xt16) {
+            // T16: the 1 KB block (16-token tile, step, half) is already in
+            // fragment order; padding bytes are zeros
+            const int64_t mb = (m0 + 16 * mc) / 16;
+            xbase[q] = mb < MB ? (uint32_t)(mb * S * 2048 + h * 1024 + 16 * lane) : kOOB;
+            xkmax[q] = (uint32_t)S;
+        } else {
+            xbase[q] = row < p.M ? (uint32_t)(row * p.ldq + k) : kOOB;
+            xkmax[q] = (uint32_t)((p.K - k + 127) / 128);     // steps with 128 s + k < K
+        }
     }
+    const uint32_t xstep = p.xt16 ? 2048u : 128u;         // bytes per 128-K step
     auto dma = [&](uint8_t *buf, int64_t s) {
         const uint32_t su = (uint32_t)s, past = su >= (uint32_t)S ? kOOB : 0u;
 #pragma unroll
@@ -106,7 +118,7 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
         for (int q = 0; q < kXq; ++q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 xr, (lds_void *)(buf + SM::kWBytes + (wave + 4 * q) * 1024), 16,
-                (int)((xbase[q] + su * 128u) | (su >= xkmax[q] ? kOOB : 0u)), 0, 0, 0);
+                (int)((xbase[q] + su * xstep) | (su >= xkmax[q] ? kOOB : 0u)), 0, 0, 0);
     };
 
     // ---- per-lane scale dwords of one quad of four steps: byte u of each

@@ -11,7 +11,7 @@ namespace mx {
 enum { E4M3 = 0, E2M1 = 1 };
 enum { ROW32 = 0, BLK32 = 1 };
 enum { RULE_OCP = 0, RULE_CEIL448 = 1 };
-enum { ACT_BF16 = 0, ACT_MXFP8 = 1 };
+enum { ACT_BF16 = 0, ACT_MXFP8 = 1, ACT_MXFP8_T16 = 2 };
 
 constexpr int kMoeMaxPairs = 4096;   // T * topk handled by one routing scan
 
@@ -36,9 +36,10 @@ struct GemvArgs {
 struct GemmArgs {
     const uint8_t *w, *codes;
     int64_t N, K, M;
-    const uint8_t *xq;
+    const uint8_t *xq;       // row-major [M, ldq], or the T16 layout when xt16
     int64_t ldq;
-    const uint8_t *xct;      // activation codes in XC-T16 order (act_codes_t16)
+    bool xt16;
+    const uint8_t *xct;      // activation codes in the T16 code layout
     const uint16_t *bias;
     uint16_t *y;
     int64_t ldy;
@@ -69,5 +70,36 @@ hipError_t launch_moe_combine(int64_t T, int64_t topk, int64_t N, const float *y
                               const float *wts, void *y, hipStream_t stream);
 hipError_t launch_gemm(int layout, const GemmArgs &a, hipStream_t stream);
 int gemm_tile_n(int64_t N);
+
+// W8A8 decode GEMV (mx_gemv_w8.hip).  Activations either row-major (xq
+// [M, ldq], codes xc [M, ldc]) or in the T16 layout (xf, xct; mx_quant.hip).
+struct GemvW8Args {
+    const uint8_t *w, *codes;      // packed weights and codes (one expert)
+    int64_t N, K, M;
+    const uint8_t *xq;
+    int64_t ldq;
+    const uint8_t *xc;
+    int64_t ldc;
+    const uint8_t *xf, *xct;
+    const uint16_t *bias;
+    uint16_t *y;
+    int64_t ldy;
+};
+// nw wavefronts per workgroup, each with at most spw steps; g tiles per
+// workgroup; ok = false if the steps do not fit the register plan
+struct GemvW8Plan {
+    int nw, spw, g;
+    bool ok;
+};
+GemvW8Plan plan_gemv_w8(int64_t T, int64_t S, int64_t MB);
+hipError_t launch_gemv_w8(int layout, bool xt16, const GemvW8Args &a, const GemvW8Plan &plan,
+                          hipStream_t stream);
+
+// per-token quantization into the T16 layout (mx_quant.hip)
+hipError_t launch_quant_t16(int64_t M, int64_t K, const void *x, int64_t ldx, void *xq,
+                            void *xc, int rule, hipStream_t stream);
+inline int64_t act_t16_data_bytes(int64_t M, int64_t K) {
+    return (M + 15) / 16 * ((K + 127) / 128) * 2048;
+}
 
 }  // namespace mx

@@ -86,6 +86,78 @@ __global__ void __launch_bounds__(256) quant_act_kernel(
     }
 }
 
+// 16-token tile ("T16") layout of a quantized activation, S = ceil(K / 128)
+// steps, Q = ceil(S / 4), MB = ceil(M / 16) tiles, lane l = 16 j + r:
+//   xq byte ((mb S + s) 2 + h) 1024 + 16 l + c
+//         = e4m3 of token 16 mb + r, K 128 s + 64 h + 16 j + c
+//           (one 1 KB block per step half, in the scaled MFMA's operand lane
+//           order: a lane's two blocks of a step are its 32 operand bytes);
+//   xc byte (mb Q + q) 256 + 4 l + u
+//         = code of token 16 mb + r, block 4 (4 q + u) + j
+//           (a lane's dword holds its codes of four steps, byte u = step 4 q + u).
+// Tokens past M, K past the end and blocks past K/32 read as byte 0 and code
+// 127, so every byte of both buffers is defined.
+//
+// One wavefront per 1 KB block (mb, s, h): lane (r, j) converts 16 values,
+// half of the 32-value block 4 s + 2 h + j / 2; the block maximum is taken
+// with the partner lane 16 apart (j xor 1).  Reads are 32 contiguous bytes per
+// lane; the write is the 1 KB block, contiguous.
+template <int RULE>
+__global__ void __launch_bounds__(256) quant_act_t16_kernel(
+    int64_t M, int64_t K, const uint16_t *__restrict__ x, int64_t ldx,
+    uint8_t *__restrict__ xq, uint8_t *__restrict__ xc, int64_t nblk) {
+    const int64_t wid = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 64;
+    if (wid >= nblk) return;                         // whole wavefronts
+    const int lane = threadIdx.x % 64, r = lane % 16, j = lane / 16;
+    const int64_t S = (K + 127) / 128, Q = (S + 3) / 4, KB = K / 32;
+    const int64_t h = wid % 2, s = (wid / 2) % S, mb = wid / (2 * S);
+    const int64_t m = 16 * mb + r, k0 = 128 * s + 64 * h + 16 * j;
+    const bool ok = m < M && k0 < K;                 // K % 32 == 0: 16 values all in or out
+    v4u v[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+    if (ok) {
+        v[0] = *reinterpret_cast<const v4u *>(x + m * ldx + k0);
+        v[1] = *reinterpret_cast<const v4u *>(x + m * ldx + k0 + 8);
+    }
+    uint32_t amax = 0;
+    for (int a = 0; a < 2; ++a)
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = (v[a][i] & 0x7FFFu) << 16, hi = (v[a][i] >> 16 & 0x7FFFu) << 16;
+            amax = amax > lo ? amax : lo;
+            amax = amax > hi ? amax : hi;
+        }
+    const uint32_t other = (uint32_t)__shfl_xor((int)amax, 16);
+    amax = amax > other ? amax : other;
+    const uint32_t code = act_code<RULE>(amax);
+    const float mul = __uint_as_float((254u - code) << 23);
+    uint32_t out[4];
+    for (int a = 0; a < 2; ++a)
+        for (int d = 0; d < 2; ++d) {
+            float f[4];
+            for (int i = 0; i < 2; ++i) {
+                const uint32_t w = v[a][2 * d + i];
+                f[2 * i] = __uint_as_float(w << 16) * mul;
+                f[2 * i + 1] = __uint_as_float(w & 0xFFFF0000u) * mul;
+            }
+            for (int i = 0; i < 4; ++i) f[i] = __builtin_fminf(__builtin_fmaxf(f[i], -448.0f), 448.0f);
+            int packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+            packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], packed, true);
+            out[2 * a + d] = (uint32_t)packed;
+        }
+    v4u o = {out[0], out[1], out[2], out[3]};
+    *reinterpret_cast<v4u *>(xq + ((mb * S + s) * 2 + h) * 1024 + 16 * lane) = o;
+    // the even lane of each pair writes the block's code
+    if (j % 2 == 0) {
+        const int64_t blk = 4 * s + 2 * h + j / 2;
+        const uint32_t c = (m < M && blk < KB) ? code : 127u;
+        xc[(mb * Q + s / 4) * 256 + 4 * (16 * (blk % 4) + r) + s % 4] = (uint8_t)c;
+    }
+    // steps 4 Q - 1 .. S are never visited: their code bytes are padding
+    if (h == 0 && s == S - 1 && j % 2 == 0)
+        for (int64_t s2 = S; s2 < 4 * Q; ++s2)
+            for (int jb = j / 2; jb < 4; jb += 2)
+                xc[(mb * Q + s2 / 4) * 256 + 4 * (16 * jb + r) + s2 % 4] = 127u;
+}
+
 hipError_t launch_quant(int64_t M, int64_t K, const void *x, int64_t ldx, void *xq, int64_t ldq,
                         void *xcodes, int64_t ldc, int rule, hipStream_t stream) {
     const int64_t threads = M * (K / 32) * 4;
@@ -96,6 +168,19 @@ hipError_t launch_quant(int64_t M, int64_t K, const void *x, int64_t ldx, void *
     else
         hipLaunchKernelGGL(quant_act_kernel<RULE_CEIL448>, grid, block, 0, stream, M, K,
                            (const uint16_t *)x, ldx, (uint8_t *)xq, ldq, (uint8_t *)xcodes, ldc);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_t16(int64_t M, int64_t K, const void *x, int64_t ldx, void *xq,
+                            void *xc, int rule, hipStream_t stream) {
+    const int64_t S = (K + 127) / 128, nblk = (M + 15) / 16 * S * 2;
+    const dim3 grid((unsigned)((nblk + 3) / 4)), block(256);
+    if (rule == RULE_OCP)
+        hipLaunchKernelGGL(quant_act_t16_kernel<RULE_OCP>, grid, block, 0, stream, M, K,
+                           (const uint16_t *)x, ldx, (uint8_t *)xq, (uint8_t *)xc, nblk);
+    else
+        hipLaunchKernelGGL(quant_act_t16_kernel<RULE_CEIL448>, grid, block, 0, stream, M, K,
+                           (const uint16_t *)x, ldx, (uint8_t *)xq, (uint8_t *)xc, nblk);
     return hipGetLastError();
 }
 

@@ -47,24 +47,51 @@ def quant(x: np.ndarray, rule: int, ldq: int | None = None):
     return xq.cpu().numpy()[:, :K], xc.cpu().numpy()
 
 
-def linear(elem, layout, N, K, wp, cp, act, x=None, xq=None, xcodes=None, rule=0, bias=None):
+def quant_t16(x: np.ndarray, rule: int):
+    """mx_quant_act_t16 of bf16 bits x [M, K]: the two device buffers."""
+    M, K = x.shape
+    qb, cb = mx.mx_act_t16_sizes(M, K)
+    xq = torch.full((qb,), 0xAB, dtype=torch.uint8, device=DEV)   # every byte must be written
+    xc = torch.full((cb,), 0xCD, dtype=torch.uint8, device=DEV)
+    mx.mx_quant_act_t16(M, K, dev(x), K, xq, xc, rule)
+    torch.cuda.synchronize()
+    return xq, xc
+
+
+def t16_unpack(xq: np.ndarray, xc: np.ndarray, M: int, K: int):
+    """The T16 layout as a reshape: data [MB][S][h][j][r][c] -> token 16 mb + r,
+    K 128 s + 64 h + 16 j + c; codes [MB][Q][j][r][u] -> token 16 mb + r, block
+    4 (4 q + u) + j.  Returns the padded row-major arrays [16 MB, 128 S] and
+    [16 MB, 16 Q]."""
+    S = -(-K // 128)
+    Q = -(-S // 4)
+    MB = -(-M // 16)
+    d = xq.reshape(MB, S, 2, 4, 16, 16).transpose(0, 4, 1, 2, 3, 5).reshape(MB * 16, S * 128)
+    c = xc.reshape(MB, Q, 4, 16, 4).transpose(0, 3, 1, 4, 2).reshape(MB * 16, Q * 16)
+    return d, c
+
+
+def linear(elem, layout, N, K, wp, cp, act, x=None, xq=None, xcodes=None, rule=0, bias=None,
+           M=None):
     """Run mx_linear; x is bf16 bits [M, K] (quantized inside the call when
-    act is MXFP8 and xq is None) or (xq, xcodes) pre-quantized."""
-    if x is not None:
-        M = x.shape[0]
-    else:
-        M = xq.shape[0]
+    act is MXFP8 and xq is None) or (xq, xcodes) pre-quantized: host arrays
+    row-major, or the device buffers of quant_t16 when act is MXFP8_T16 (then
+    M is given)."""
+    if M is None:
+        M = x.shape[0] if x is not None else xq.shape[0]
     y = torch.empty((M, N), dtype=torch.int16, device=DEV)
     xd = dev(x) if x is not None else None
     xqd = xcd = None
     ldq = ldc = 0
-    if xq is not None:
+    if act == mx.MX_ACT_MXFP8_T16:
+        xqd, xcd = xq, xcodes                       # device buffers of quant_t16
+    elif xq is not None:
         ldq = (K + 15) // 16 * 16
         buf = np.zeros((M, ldq), np.uint8)
         buf[:, :K] = xq
         xqd, xcd, ldc = dev(buf), dev(xcodes), xcodes.shape[1]
     need = mx.mx_linear_workspace(elem, layout, N, K, M, act, xq is not None)
-    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=DEV)
     bd = dev(bias) if bias is not None else None
     mx.mx_linear(elem, layout, N, K, wp, cp, M, act, rule, xd, K if x is not None else 0,
                  xqd, ldq, xcd, ldc, bd, y, N, ws, need)
@@ -77,7 +104,7 @@ def moe(elem, E, N, K, wp, cp, x, ids, weights=None):
     combine = weights is not None
     y = torch.empty((T, N) if combine else (T, topk, N), dtype=torch.int16, device=DEV)
     need = mx.mx_moe_workspace(elem, E, N, K, T, topk, combine)
-    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=DEV)
     mx.mx_moe_linear(elem, E, N, K, wp, cp, T, topk, dev(x), K, dev(ids),
                      dev(weights) if combine else None, y, ws, need)
     torch.cuda.synchronize()

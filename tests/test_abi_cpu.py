@@ -85,7 +85,10 @@ def test_linear_validation_paths():
     assert _linear(layout=1, N=48) == SHAPE
     assert _linear(elem=1, act=1) == UNSUP
     assert _linear(elem=1, layout=1) == UNSUP
-    assert _linear(act=2) == UNSUP
+    assert _linear(act=3) == UNSUP
+    # T16 activations: both buffers required, 16-byte aligned
+    assert _linear(act=2) == NULL
+    assert _linear(act=2, x=None, xq=A, xc=A + 4) == ALIGN
     assert _linear(rule=3) == UNSUP
     assert _linear(x=None) == NULL
     assert _linear(y=None) == NULL
@@ -99,14 +102,37 @@ def test_linear_validation_paths():
     need = mx.mx_linear_workspace(0, 0, 64, 256, 4, 1, 0)
     assert need >= 4 * 256 + 4 * 8
     assert _linear(act=1, ws=A, wsb=need - 1) == WS
-    # pre-quantized activations: strides checked
+    # pre-quantized activations: strides checked; the decode GEMV needs no
+    # workspace for them, nor for bf16 activations
     assert _linear(act=1, x=None, xq=A, ldq=256, xc=A, ldc=4) == SHAPE
     assert _linear(act=1, x=None, xq=A, ldq=264, xc=A, ldc=8) == ALIGN
+    assert mx.mx_linear_workspace(0, 0, 64, 256, 4, 1, 1) == 0
+    assert mx.mx_linear_workspace(0, 0, 64, 256, 4, 0, 0) == 0
+    # the prefill GEMM restages the activation codes even when pre-quantized
+    assert mx.mx_linear_workspace(0, 0, 64, 256, 65, 1, 1) > 0
     # a valid call on a machine without a gfx950 device stops at the gate
     import torch
     if not torch.cuda.is_available():
         assert _linear() == DEVICE
         assert _linear(act=1, x=None, xq=A, ldq=256, xc=A, ldc=8) == DEVICE
+
+
+def test_t16_sizes_and_quant_validation():
+    # S = ceil(K / 128) steps, Q = ceil(S / 4), MB = ceil(M / 16)
+    for M, K in [(1, 128), (16, 7168), (17, 160), (64, 1568)]:
+        S = -(-K // 128)
+        Q = -(-S // 4)
+        MB = -(-M // 16)
+        assert mx.mx_act_t16_sizes(M, K) == (MB * S * 2048, MB * Q * 256)
+    L = mx.lib()
+    qb, cb = C.c_size_t(), C.c_size_t()
+    assert L.mx_act_t16_sizes(0, 128, C.byref(qb), C.byref(cb)) == SHAPE
+    assert L.mx_act_t16_sizes(4, 100, C.byref(qb), C.byref(cb)) == SHAPE
+    assert L.mx_act_t16_sizes(4, 128, None, C.byref(cb)) == NULL
+    assert L.mx_quant_act_t16(4, 128, A, 120, A, A, 0, None) == SHAPE
+    assert L.mx_quant_act_t16(4, 128, None, 128, A, A, 0, None) == NULL
+    assert L.mx_quant_act_t16(4, 128, A, 128, A, A + 8, 0, None) == ALIGN
+    assert L.mx_quant_act_t16(4, 128, A, 128, A, A, 5, None) == UNSUP
 
 
 def test_quant_and_pack_and_moe_validation_paths():

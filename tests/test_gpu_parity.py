@@ -14,7 +14,7 @@ from microscaling_quantized_linear_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 E4M3, E2M1, ROW32, BLK32 = 0, 1, 0, 1
-BF16, MXFP8, OCP, CEIL = 0, 1, 0, 1
+BF16, MXFP8, MXFP8_T16, OCP, CEIL = 0, 1, 2, 0, 1
 
 
 @pytest.fixture(scope="module")
@@ -305,3 +305,42 @@ def test_moe_e4m3_weights(g):
     ref = oracle.moe_linear(E4M3, E, N, K, w, codes, x, ids)
     y = g.moe(E4M3, E, N, K, wp, cp, x, ids)
     g.assert_close(y, ref, "moe e4m3")
+
+
+# ------------------------------------------------- T16 activation layout
+
+T16_SHAPES = [(1, 128), (3, 160), (16, 7168), (17, 1568), (64, 512), (300, 384)]
+
+
+@pytest.mark.parametrize("rule", [OCP, CEIL])
+@pytest.mark.parametrize("M,K", T16_SHAPES)
+def test_quant_t16_bit_exact(g, rule, M, K):
+    """mx_quant_act_t16 holds exactly the oracle's bytes and codes, in the
+    documented layout; padding tokens and K hold byte 0 and code 127."""
+    x = wl.activations(np.random.default_rng([43, M, K]), (M, K), 0.02)
+    xq, xc = g.quant_t16(x, rule)
+    d, c = g.t16_unpack(xq.cpu().numpy(), xc.cpu().numpy(), M, K)
+    oq, oc = oracle.quant_act(x, rule)
+    np.testing.assert_array_equal(d[:M, :K], oq)
+    np.testing.assert_array_equal(c[:M, :K // 32], oc)
+    assert not d[M:].any() and not d[:, K:].any()
+    assert (c[M:] == 127).all() and (c[:, K // 32:] == 127).all()
+
+
+@pytest.mark.parametrize("layout", [ROW32, BLK32])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (5, 96, 1568), (16, 256, 7168), (40, 64, 384),
+                                   (300, 256, 384)])
+def test_linear_t16_equals_in_call(g, layout, M, N, K):
+    """A linear on a T16 activation gives the in-call result bit for bit
+    (decode GEMV for M <= 64, prefill GEMM above), within the bar of the
+    oracle."""
+    w, codes, x, bias = _dense_inputs([44, M, N, K, layout], E4M3, layout, M, N, K)
+    wp, cp = g.pack(E4M3, layout, 1, N, K, w, codes)
+    b = bias if M % 2 else None
+    xq, xc = g.quant_t16(x, OCP)
+    y = g.linear(E4M3, layout, N, K, wp, cp, MXFP8_T16, xq=xq, xcodes=xc, bias=b, M=M)
+    y_in = g.linear(E4M3, layout, N, K, wp, cp, MXFP8, x=x, rule=OCP, bias=b)
+    assert np.array_equal(y, y_in)
+    oq, oc = oracle.quant_act(x, OCP)
+    ref = oracle.linear(E4M3, layout, N, K, w, codes, M, MXFP8, xq=oq, xcodes=oc, bias=b)
+    g.assert_close(y, ref, "T16 activation")
