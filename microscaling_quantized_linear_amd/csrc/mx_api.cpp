@@ -31,8 +31,15 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 
 // the W8A8 GEMV's launch plan (fails for more than 64 steps of K per wavefront)
+int env_int(const char *name) {
+    const char *s = std::getenv(name);
+    return s ? std::atoi(s) : 0;
+}
+
+// MX_W8_WAVES and MX_W8_TILES override the plan (tuning sweeps only; read once)
 mx::GemvW8Plan gemv_w8_plan(int64_t N, int64_t K, int64_t M) {
-    return mx::plan_gemv_w8(N / 16, (K + 127) / 128, (M + 15) / 16);
+    static const int f_nw = env_int("MX_W8_WAVES"), f_g = env_int("MX_W8_TILES");
+    return mx::plan_gemv_w8(N / 16, (K + 127) / 128, (M + 15) / 16, f_nw, f_g);
 }
 int64_t padded_k(int64_t K) { return (K + 127) / 128 * 128; }
 

@@ -221,6 +221,12 @@ static hipError_t launch_w8_spw(const GemvW8Args &a, const GemvW8Plan &pl, hipSt
     case 1: hipLaunchKernelGGL((gemv_w8_kernel<LAYOUT, XFRAG, G, 1>), grid, block, 0, st, a); break;
     case 2: hipLaunchKernelGGL((gemv_w8_kernel<LAYOUT, XFRAG, G, 2>), grid, block, 0, st, a); break;
     case 4: hipLaunchKernelGGL((gemv_w8_kernel<LAYOUT, XFRAG, G, 4>), grid, block, 0, st, a); break;
+    case 7:
+        if constexpr (G * 7 <= 16)
+            hipLaunchKernelGGL((gemv_w8_kernel<LAYOUT, XFRAG, G, 7>), grid, block, 0, st, a);
+        else
+            return hipErrorInvalidValue;
+        break;
     default:
         // the plan keeps G * SPW <= 16 (registers)
         if constexpr (G * 8 <= 16)
@@ -251,14 +257,16 @@ hipError_t launch_gemv_w8(int layout, bool xfrag, const GemvW8Args &a, const Gem
 // Launch plan for T tiles, S steps and MB 16-token grid rows: tiles per
 // workgroup G in {4, 2, 1} (the largest that still gives about one
 // workgroup per compute unit, measured best on MI355X), up to eight
-// wavefronts per workgroup, each with at most SPW in {1, 2, 4, 8} steps.
-// ok = false when S needs more than 64 steps' worth of registers.
-GemvW8Plan plan_gemv_w8(int64_t T, int64_t S, int64_t MB) {
+// wavefronts per workgroup, each with at most SPW in {1, 2, 4, 7, 8} steps.
+// ok = false when S needs more than 64 steps' worth of registers.  nw_force
+// and g_force (0 = none) override the choice, for tuning sweeps.
+GemvW8Plan plan_gemv_w8(int64_t T, int64_t S, int64_t MB, int nw_force, int g_force) {
     GemvW8Plan pl{};
-    const int nw = S >= 8 ? 8 : (int)S;
+    int nw = S >= 8 ? 8 : (int)S;
+    if (nw_force >= 1 && nw_force <= 8) nw = nw_force;
     const int64_t per = (S + nw - 1) / nw;
     pl.nw = nw;
-    pl.spw = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : 8;
+    pl.spw = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per == 7 ? 7 : 8;
     pl.ok = per <= 8;
     pl.g = 1;
     for (int g : {4, 2}) {
@@ -268,6 +276,7 @@ GemvW8Plan plan_gemv_w8(int64_t T, int64_t S, int64_t MB) {
             break;
         }
     }
+    if ((g_force == 1 || g_force == 2 || g_force == 4) && g_force * pl.spw <= 16) pl.g = g_force;
     return pl;
 }
 

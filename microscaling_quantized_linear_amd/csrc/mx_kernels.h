@@ -91,7 +91,7 @@ struct GemvW8Plan {
     int nw, spw, g;
     bool ok;
 };
-GemvW8Plan plan_gemv_w8(int64_t T, int64_t S, int64_t MB);
+GemvW8Plan plan_gemv_w8(int64_t T, int64_t S, int64_t MB, int nw_force, int g_force);
 hipError_t launch_gemv_w8(int layout, bool xt16, const GemvW8Args &a, const GemvW8Plan &plan,
                           hipStream_t stream);
 
