@@ -161,26 +161,32 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
         constexpr int U = decltype(uconst)::value;
         dma(nxt, s + 1);
         __builtin_amdgcn_sched_barrier(0);
-        v8i bf[8];
+        // the activation fragments and the first weight fragment are read
+        // first; each later weight fragment is read one group of MFMAs ahead
+        // of its use, so LDS latency overlaps the matrix cores
+        v8i af[2], bf[8];
+        auto read_a = [&](int nt, v8i &dst) {
+            const uint8_t *cp = cur + (wn * NTW + nt) * 2048;
+            dst = cat8(*reinterpret_cast<const v4u *>(cp + 16 * lane),
+                       *reinterpret_cast<const v4u *>(cp + 1024 + 16 * lane));
+        };
+        read_a(0, af[0]);
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             const uint8_t *cp = cur + SM::kWBytes + (wm * 8 + mt) * 2048;
             bf[mt] = cat8(*reinterpret_cast<const v4u *>(cp + 16 * lane),
                           *reinterpret_cast<const v4u *>(cp + 1024 + 16 * lane));
         }
-        v8i af[NTW];
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
-            const uint8_t *cp = cur + (wn * NTW + nt) * 2048;
-            af[nt] = cat8(*reinterpret_cast<const v4u *>(cp + 16 * lane),
-                          *reinterpret_cast<const v4u *>(cp + 1024 + 16 * lane));
-        }
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt)
+            if (nt + 1 < NTW) read_a(nt + 1, af[(nt + 1) % 2]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt)
-                acc[nt][mt] = mfma_fp8_scaled_sel<U>(af[nt], bf[mt], acc[nt][mt], (int)sc.w[nt],
-                                                     (int)sc.x[mt]);
+                acc[nt][mt] = mfma_fp8_scaled_sel<U>(af[nt % 2], bf[mt], acc[nt][mt],
+                                                     (int)sc.w[nt], (int)sc.x[mt]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
     };
