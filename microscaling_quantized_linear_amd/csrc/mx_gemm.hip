@@ -4,19 +4,22 @@
 // block scales consumed directly by the CDNA4 microscaling matrix cores,
 // activations quantized per token with row-major codes.)
 //
-// Workgroup tile: BN weight rows x 256 tokens, 4 wavefronts as 2 x 2, each
-// wavefront NTW x 8 tiles of 16 x 16 accumulated by
-// v_mfma_scale_f32_16x16x128_f8f6f4 (A = weights, B = activations, both
-// with per-lane E8M0 scales).  Per 128-K step the workgroup copies its
-// weight chunks (W-T16: each 2 KB chunk is already one operand in lane
-// order) and its activation rows (already in fragment order when they come
-// in the T16 layout, else rearranged into it by the copy's addressing)
-// straight from memory into one of two LDS
-// buffers (buffer loads with an LDS destination) while the matrix cores
-// work on the other; one barrier per step.  Scale codes are read once per
-// four steps as one dword per lane (byte u = step 4q + u) and the MFMA's
-// byte select picks the step's code.  Out-of-range rows and K tails read
-// zeros through buffer-resource bounds.
+// Workgroup tile: BN weight rows x 256 tokens, 4 wavefronts side by side
+// along the tokens: each wavefront owns all BN rows and 64 tokens, NTW x 2
+// output tiles of 32 x 32 accumulated by v_mfma_scale_f32_32x32x64_f8f6f4
+// (A = weights, B = activations, both with per-lane E8M0 scales).  On
+// MI355X the 32 x 32 x 64 form issues at its full rate (64 cycles for 2^17
+// flop); the 16 x 16 x 128 form measured about 41 cycles for half as many.
+// Per 128-K step the workgroup copies its weight chunks (W-T16, 2 KB per 16
+// rows) and its activation rows (already in fragment order when they come in
+// the T16 layout, else rearranged into it by the copy's addressing) straight
+// from memory into one of two LDS buffers (buffer loads with an LDS
+// destination) while the matrix cores work on the other; one barrier per
+// step.  A 32 x 32 x 64 operand lane (row r, K group g) reads its two
+// 16-byte pieces from those 16-row chunks.  Scale codes are read once per
+// four steps as dwords whose byte u is step 4q + u's code, picked by the
+// MFMA's byte select.  Out-of-range rows and K tails read zeros through
+// buffer-resource bounds.
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -46,11 +49,12 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     // the operand reads of the other and waits only where it must
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[SM::kBuf];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[SM::kBuf];
-    constexpr int BN = 2 * NTW * 16;
+    constexpr int BN = NTW * 32;
     const int tid = threadIdx.x, lane = tid % 64;
-    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    // bounded so the compiler can tell the two LDS buffers' accesses apart
+    // (otherwise it waits for the next step's copies before reading this one)
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64) & 3;
     const int r = lane % 16, j = lane / 16;
-    const int wn = wave % 2, wm = wave / 2;
     const int64_t Kp = (p.K + 127) / 128 * 128, S = Kp / 128, T = p.N / 16, Q = (S + 3) / 4;
     const int64_t KB = p.K / 32;
 
@@ -107,87 +111,133 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
         }
     }
     const uint32_t xstep = p.xt16 ? 2048u : 128u;         // bytes per 128-K step
-    auto dma = [&](uint8_t *buf, int64_t s) {
-        const uint32_t su = (uint32_t)s, past = su >= (uint32_t)S ? kOOB : 0u;
-#pragma unroll
-        for (int q = 0; q < kWq; ++q)
+    // copy i of step s into buf: i < kWq weight chunk-halves, then activation ones
+    constexpr int kCopies = kWq + kXq;
+    auto dma_one = [&](uint8_t *buf, int64_t s, int i) {
+        const uint32_t su = (uint32_t)s;
+        if (i < kWq) {
+            const uint32_t past = su >= (uint32_t)S ? kOOB : 0u;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                wr, (lds_void *)(buf + (wave + 4 * q) * 1024), 16,
-                (int)((wbase[q] + su * 2048u) | past), 0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < kXq; ++q)
+                wr, (lds_void *)(buf + (wave + 4 * i) * 1024), 16,
+                (int)((wbase[i] + su * 2048u) | past), 0, 0, 0);
+        } else {
+            const int q = i - kWq;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 xr, (lds_void *)(buf + SM::kWBytes + (wave + 4 * q) * 1024), 16,
                 (int)((xbase[q] + su * xstep) | (su >= xkmax[q] ? kOOB : 0u)), 0, 0, 0);
+        }
+    };
+    auto dma = [&](uint8_t *buf, int64_t s) {
+#pragma unroll
+        for (int i = 0; i < kCopies; ++i) dma_one(buf, s, i);
     };
 
+    // ---- 32 x 32 x 64 operands: lane (g, rr) = lane / 32, lane % 32 holds
+    // row rr with K 16 g .. and 32 + 16 g .. of a 64-K half-step kh; in the
+    // 16-row chunks that is chunk 2 T + rr / 16, bytes 1024 kh + 256 g +
+    // 16 (rr % 16) and 512 further ----
+    const int rr = lane % 32, g = lane / 32;
+    const int off_lane = (rr / 16) * 2048 + 256 * g + 16 * (rr % 16);
+
     // ---- per-lane scale dwords of one quad of four steps: byte u of each
-    // dword is step 4 q + u's code, picked by the MFMA's opsel ----
+    // dword is step 4 q + u's code, picked by the MFMA's opsel; lane (g, rr)
+    // of half-step kh needs block 2 kh + g of its row ----
     struct QScales {
-        uint32_t w[NTW], x[8];
+        uint32_t w[NTW][2], x[2][2];
     };
-    uint32_t cwbase[NTW], cxbase[8];
+    uint32_t cwbase[NTW][2], cxbase[2][2];
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-        const int64_t t = t0 + wn * NTW + nt;
-        if (LAYOUT == ROW32)
-            cwbase[nt] = t < T ? (uint32_t)(t * Q * 256 + 4 * lane) : kOOB;
-        else
-            cwbase[nt] = t < T ? (uint32_t)(((16 * t) / 32) * Q * 16 + 4 * j) : kOOB;
-    }
+    for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-        const int64_t row0 = m0 + wm * 128 + 16 * mt;     // XC-T16 tile of 16 rows
-        cxbase[mt] = row0 < p.M ? (uint32_t)((row0 / 16) * Q * 256 + 4 * lane) : kOOB;
-    }
+        for (int kh = 0; kh < 2; ++kh) {
+            const int jb = 2 * kh + g;                    // block of the 128-K step
+            const int64_t row = n0 + 32 * nt + rr;
+            if (LAYOUT == ROW32)
+                cwbase[nt][kh] = row < p.N ? (uint32_t)((row / 16) * Q * 256 +
+                                                        4 * (16 * jb + row % 16)) : kOOB;
+            else
+                cwbase[nt][kh] = row < p.N ? (uint32_t)((row / 32) * Q * 16 + 4 * jb) : kOOB;
+        }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+            const int jb = 2 * kh + g;
+            const int64_t tok = m0 + 64 * wave + 32 * mt + rr;    // T16 code layout
+            cxbase[mt][kh] = tok < 16 * MB ? (uint32_t)((tok / 16) * Q * 256 +
+                                                         4 * (16 * jb + tok % 16)) : kOOB;
+        }
     auto load_qscales = [&](int64_t q, QScales &out) {
         const uint32_t qu = (uint32_t)q, past = qu >= (uint32_t)Q ? kOOB : 0u;
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt)
-            out.w[nt] = load4(cr, (cwbase[nt] + qu * (LAYOUT == ROW32 ? 256u : 16u)) | past);
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) out.x[mt] = load4(xcr, (cxbase[mt] + qu * 256u) | past);
+            for (int kh = 0; kh < 2; ++kh)
+                out.w[nt][kh] = load4(cr, (cwbase[nt][kh] + qu * (LAYOUT == ROW32 ? 256u : 16u)) | past);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+                out.x[mt][kh] = load4(xcr, (cxbase[mt][kh] + qu * 256u) | past);
     };
 
-    v4f acc[NTW][8];
+    typedef float v16f __attribute__((ext_vector_type(16)));
+    v16f acc[NTW][2];
 #pragma unroll
     for (int a = 0; a < NTW; ++a)
 #pragma unroll
-        for (int b = 0; b < 8; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
-    // one 128-K step, step u of its quad: DMA of step s + 1 into `nxt`, then
-    // the MFMAs of step s from `cur` with the quad's scales `sc`
+    // one 128-K step, step u of its quad: the MFMAs of step s from `cur` with
+    // the quad's scales `sc`, interleaved with the copies of step s + 1 into
+    // `nxt`.  The 2 NTW
+    // MFMA groups (half-step kh, weight tile nt) each take two MFMAs; a
+    // group's weight fragment is read two groups ahead, the activation
+    // fragments of a half-step with the reads of its first groups.
     auto step = [&](uint8_t *cur, uint8_t *nxt, int64_t s, const QScales &sc, auto uconst) {
         constexpr int U = decltype(uconst)::value;
-        dma(nxt, s + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        // the activation fragments and the first weight fragment are read
-        // first; each later weight fragment is read one group of MFMAs ahead
-        // of its use, so LDS latency overlaps the matrix cores
-        v8i af[2], bf[8];
-        auto read_a = [&](int nt, v8i &dst) {
-            const uint8_t *cp = cur + (wn * NTW + nt) * 2048;
-            dst = cat8(*reinterpret_cast<const v4u *>(cp + 16 * lane),
-                       *reinterpret_cast<const v4u *>(cp + 1024 + 16 * lane));
+        auto rd = [&](const uint8_t *base, int kh) -> v8i {
+            const uint8_t *cp = base + off_lane + 1024 * kh;
+            return cat8(*reinterpret_cast<const v4u *>(cp),
+                        *reinterpret_cast<const v4u *>(cp + 512));
         };
-        read_a(0, af[0]);
+        const uint8_t *wb = cur, *xb = cur + SM::kWBytes + (4 * wave) * 2048;
+        constexpr int NG = 2 * NTW;                       // groups (kh, nt), kh major
+        v8i af[3], bf[2][2];
+        auto issue = [&](int k) {                         // the reads group k needs first
+            const int kh = k / NTW, nt = k % NTW;
+            if (nt == 0) {
+                bf[kh][0] = rd(xb, kh);
+                bf[kh][1] = rd(xb + 2 * 2048, kh);
+            }
+            af[k % 3] = rd(wb + 2 * nt * 2048, kh);
+        };
+        issue(0);
+        issue(1);
+        // the copies of step s + 1 go out two per MFMA group from the top of
+        // the step: issued all at once, the four wavefronts' 60 KB queue on
+        // the CU's address path (64 B/clock) and hold back the MFMAs; spread,
+        // the copies and the matrix cores overlap and the last copy still has
+        // half a step to land before the barrier
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const uint8_t *cp = cur + SM::kWBytes + (wm * 8 + mt) * 2048;
-            bf[mt] = cat8(*reinterpret_cast<const v4u *>(cp + 16 * lane),
-                          *reinterpret_cast<const v4u *>(cp + 1024 + 16 * lane));
-        }
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-            if (nt + 1 < NTW) read_a(nt + 1, af[(nt + 1) % 2]);
+        for (int k = 0; k < NG; ++k) {
+            if (2 * k < kCopies) dma_one(nxt, s + 1, 2 * k);
+            if (2 * k + 1 < kCopies) dma_one(nxt, s + 1, 2 * k + 1);
+            if (k + 2 < NG) issue(k + 2);
             __builtin_amdgcn_sched_barrier(0);
+            const int kh = k / NTW, nt = k % NTW;
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
-                acc[nt][mt] = mfma_fp8_scaled_sel<U>(af[nt % 2], bf[mt], acc[nt][mt],
-                                                     (int)sc.w[nt], (int)sc.x[mt]);
+            for (int mt = 0; mt < 2; ++mt)
+                acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    af[k % 3], bf[kh][mt], acc[nt][mt], 0, 0, U, (int)sc.w[nt][kh], U,
+                    (int)sc.x[mt][kh]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        // this wavefront's copies of step s + 1 have landed before any
+        // wavefront reads them
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
         __syncthreads();
     };
     using U0 = std::integral_constant<int, 0>;
@@ -216,29 +266,46 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
         step(lds1, lds0, s + 7, qb, U3{});
     }
 
-    // ---- epilogue: lane (r, j) of tile (nt, mt) holds n = 4 j .. 4 j + 3, m = r ----
+    // ---- epilogue, through LDS (both buffers are free after the last
+    // step's barrier): each wavefront writes its BN x 64 outputs, bias added
+    // and rounded to bf16, as 64 token rows of BN values into its own region,
+    // then stores whole rows, consecutive lanes on consecutive 16 bytes.
+    // Element i of lane (g, rr) in tile (nt, mt) is weight row
+    // 32 nt + 8 (i / 4) + 4 g + i % 4 and token 32 mt + rr. ----
+    // bytes per staged row, padded by 16 where two wavefronts' rows still
+    // fit one buffer (fewer bank conflicts on the row writes)
+    constexpr int kRow = 2 * 64 * (BN * 2 + 16) <= SM::kBuf ? BN * 2 + 16 : BN * 2;
+    static_assert(2 * 64 * kRow <= SM::kBuf, "two wavefronts' rows fit one buffer");
+    uint8_t *stage = (wave < 2 ? lds0 : lds1) + (wave % 2) * 64 * kRow;
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-        const int64_t n = n0 + (wn * NTW + nt) * 16 + 4 * j;
-        if (n >= p.N) continue;
-        float bv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (p.bias)
-            for (int i = 0; i < 4; ++i) bv[i] = bf16_to_f32(p.bias[n + i]);
+    for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const int64_t m = m0 + wm * 128 + 16 * mt + r;
-            if (m >= p.M) continue;
-            const v4f a = acc[nt][mt];
-            v2u o = {bf16_bits(a[0] + bv[0]) | (bf16_bits(a[1] + bv[1]) << 16),
-                     bf16_bits(a[2] + bv[2]) | (bf16_bits(a[3] + bv[3]) << 16)};
-            *reinterpret_cast<v2u *>(p.y + m * p.ldy + n) = o;
+        for (int a = 0; a < 4; ++a) {
+            const int nl = 32 * nt + 8 * a + 4 * g;
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (p.bias && n0 + nl < p.N)
+                for (int i = 0; i < 4; ++i) bv[i] = bf16_to_f32(p.bias[n0 + nl + i]);
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                const v16f &c = acc[nt][mt];
+                v2u o = {bf16_bits(c[4 * a] + bv[0]) | (bf16_bits(c[4 * a + 1] + bv[1]) << 16),
+                         bf16_bits(c[4 * a + 2] + bv[2]) | (bf16_bits(c[4 * a + 3] + bv[3]) << 16)};
+                *reinterpret_cast<v2u *>(stage + (32 * mt + rr) * kRow + 2 * nl) = o;
+            }
         }
+    constexpr int kChunks = BN * 2 / 16;                  // 16-byte pieces per row
+#pragma unroll 4
+    for (int c = lane; c < 64 * kChunks; c += 64) {
+        const int row = c / kChunks, piece = c % kChunks;
+        const int64_t m = m0 + 64 * wave + row, n = n0 + 8 * piece;
+        const v4u v = *reinterpret_cast<const v4u *>(stage + row * kRow + 16 * piece);
+        if (m < p.M && n < p.N) *reinterpret_cast<v4u *>(p.y + m * p.ldy + n) = v;
     }
 }
 
 template <int LAYOUT, int NTW>
 static hipError_t launch_ntw(const GemmArgs &a, hipStream_t st) {
-    constexpr int BN = 2 * NTW * 16;
+    constexpr int BN = NTW * 32;
     const int64_t tiles = ((a.N + BN - 1) / BN) * ((a.M + kBM - 1) / kBM);
     hipLaunchKernelGGL((gemm_w8a8_kernel<LAYOUT, NTW>), dim3((unsigned)tiles), dim3(256), 0, st,
                        a);
