@@ -97,7 +97,9 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     }
 #pragma unroll
     for (int q = 0; q < kXq; ++q) {
-        const int i = wave + 4 * q, mc = i / 2, h = i % 2;
+        // wavefront w copies its own 64 tokens: chunks 4 w .. 4 w + 3, both
+        // halves (chunk-half 8 w + q), so it may read them without a barrier
+        const int i = 8 * wave + q, mc = i / 2, h = i % 2;
         const int64_t row = m0 + 16 * mc + r, k = 64 * h + 16 * j;
         if (p.xt16) {
             // T16: the 1 KB block (16-token tile, step, half) is already in
@@ -123,7 +125,7 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
         } else {
             const int q = i - kWq;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xr, (lds_void *)(buf + SM::kWBytes + (wave + 4 * q) * 1024), 16,
+                xr, (lds_void *)(buf + SM::kWBytes + (8 * wave + q) * 1024), 16,
                 (int)((xbase[q] + su * xstep) | (su >= xkmax[q] ? kOOB : 0u)), 0, 0, 0);
         }
     };
@@ -196,23 +198,28 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     // MFMA groups (half-step kh, weight tile nt) each take two MFMAs; a
     // group's weight fragment is read two groups ahead, the activation
     // fragments of a half-step with the reads of its first groups.
+    auto rd = [&](const uint8_t *base, int kh) -> v8i {
+        const uint8_t *cp = base + off_lane + 1024 * kh;
+        return cat8(*reinterpret_cast<const v4u *>(cp), *reinterpret_cast<const v4u *>(cp + 512));
+    };
+    // the wavefront's activation fragments of one step (both half-steps);
+    // this wavefront alone copies them, so they are read as soon as its own
+    // copies have landed, before the barrier
+    v8i bf[2][2];
+    auto read_b = [&](const uint8_t *buf) {
+        const uint8_t *xb = buf + SM::kWBytes + (4 * wave) * 2048;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) bf[kh][mt] = rd(xb + 2 * mt * 2048, kh);
+    };
     auto step = [&](uint8_t *cur, uint8_t *nxt, int64_t s, const QScales &sc, auto uconst) {
         constexpr int U = decltype(uconst)::value;
-        auto rd = [&](const uint8_t *base, int kh) -> v8i {
-            const uint8_t *cp = base + off_lane + 1024 * kh;
-            return cat8(*reinterpret_cast<const v4u *>(cp),
-                        *reinterpret_cast<const v4u *>(cp + 512));
-        };
-        const uint8_t *wb = cur, *xb = cur + SM::kWBytes + (4 * wave) * 2048;
+        const uint8_t *wb = cur;
         constexpr int NG = 2 * NTW;                       // groups (kh, nt), kh major
-        v8i af[3], bf[2][2];
-        auto issue = [&](int k) {                         // the reads group k needs first
-            const int kh = k / NTW, nt = k % NTW;
-            if (nt == 0) {
-                bf[kh][0] = rd(xb, kh);
-                bf[kh][1] = rd(xb + 2 * 2048, kh);
-            }
-            af[k % 3] = rd(wb + 2 * nt * 2048, kh);
+        v8i af[3];
+        auto issue = [&](int k) {                         // group k's weight fragment
+            af[k % 3] = rd(wb + 2 * (k % NTW) * 2048, k / NTW);
         };
         issue(0);
         issue(1);
@@ -238,6 +245,7 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
         // this wavefront's copies of step s + 1 have landed before any
         // wavefront reads them
         __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+        read_b(nxt);
         __syncthreads();
     };
     using U0 = std::integral_constant<int, 0>;
@@ -248,7 +256,9 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     QScales qa, qb;
     dma(lds0, 0);
     load_qscales(0, qa);
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
     __syncthreads();
+    read_b(lds0);
     // eight steps (two quads) per iteration: each LDS buffer is a fixed object
     // and the two scale sets alternate without copies; a step at or past S
     // reads zeros and adds nothing
