@@ -50,6 +50,8 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[SM::kBuf];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[SM::kBuf];
     constexpr int BN = NTW * 32;
+    static_assert(BN <= 256, "one bias value per thread");
+    __shared__ __attribute__((aligned(16))) uint16_t bias_lds[BN];
     const int tid = threadIdx.x, lane = tid % 64;
     // bounded so the compiler can tell the two LDS buffers' accesses apart
     // (otherwise it waits for the next step's copies before reading this one)
@@ -184,13 +186,8 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     };
 
     typedef float v16f __attribute__((ext_vector_type(16)));
+    // first written by the first step's MFMAs, which take a zero C operand
     v16f acc[NTW][2];
-#pragma unroll
-    for (int a = 0; a < NTW; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
     // one 128-K step, step u of its quad: the MFMAs of step s from `cur` with
     // the quad's scales `sc`, interleaved with the copies of step s + 1 into
@@ -213,8 +210,10 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) bf[kh][mt] = rd(xb + 2 * mt * 2048, kh);
     };
-    auto step = [&](uint8_t *cur, uint8_t *nxt, int64_t s, const QScales &sc, auto uconst) {
+    auto step = [&](uint8_t *cur, uint8_t *nxt, int64_t s, const QScales &sc, auto uconst,
+                    auto firstconst) {
         constexpr int U = decltype(uconst)::value;
+        constexpr bool kFirst = decltype(firstconst)::value;
         const uint8_t *wb = cur;
         constexpr int NG = 2 * NTW;                       // groups (kh, nt), kh major
         v8i af[3];
@@ -238,8 +237,8 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
                 acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    af[k % 3], bf[kh][mt], acc[nt][mt], 0, 0, U, (int)sc.w[nt][kh], U,
-                    (int)sc.x[mt][kh]);
+                    af[k % 3], bf[kh][mt], kFirst && kh == 0 ? v16f{} : acc[nt][mt], 0, 0, U,
+                    (int)sc.w[nt][kh], U, (int)sc.x[mt][kh]);
             __builtin_amdgcn_sched_barrier(0);
         }
         // this wavefront's copies of step s + 1 have landed before any
@@ -252,6 +251,11 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     using U1 = std::integral_constant<int, 1>;
     using U2 = std::integral_constant<int, 2>;
     using U3 = std::integral_constant<int, 3>;
+    using F0 = std::false_type;
+
+    // the workgroup's BN bias values, staged in LDS under the first barrier
+    // (the bias needs only 2-byte alignment: one element per thread)
+    if (p.bias && tid < BN) bias_lds[tid] = n0 + tid < p.N ? p.bias[n0 + tid] : 0;
 
     QScales qa, qb;
     dma(lds0, 0);
@@ -265,52 +269,85 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     for (int64_t s = 0; s < S; s += 8) {
         const int64_t q = s / 4;
         load_qscales(q + 1, qb);
-        step(lds0, lds1, s + 0, qa, U0{});
-        step(lds1, lds0, s + 1, qa, U1{});
-        step(lds0, lds1, s + 2, qa, U2{});
-        step(lds1, lds0, s + 3, qa, U3{});
+        if (s == 0)
+            step(lds0, lds1, s + 0, qa, U0{}, std::true_type{});
+        else
+            step(lds0, lds1, s + 0, qa, U0{}, F0{});
+        step(lds1, lds0, s + 1, qa, U1{}, F0{});
+        step(lds0, lds1, s + 2, qa, U2{}, F0{});
+        step(lds1, lds0, s + 3, qa, U3{}, F0{});
         load_qscales(q + 2, qa);
-        step(lds0, lds1, s + 4, qb, U0{});
-        step(lds1, lds0, s + 5, qb, U1{});
-        step(lds0, lds1, s + 6, qb, U2{});
-        step(lds1, lds0, s + 7, qb, U3{});
+        step(lds0, lds1, s + 4, qb, U0{}, F0{});
+        step(lds1, lds0, s + 5, qb, U1{}, F0{});
+        step(lds0, lds1, s + 6, qb, U2{}, F0{});
+        step(lds1, lds0, s + 7, qb, U3{}, F0{});
     }
 
-    // ---- epilogue, through LDS (both buffers are free after the last
-    // step's barrier): each wavefront writes its BN x 64 outputs, bias added
-    // and rounded to bf16, as 64 token rows of BN values into its own region,
-    // then stores whole rows, consecutive lanes on consecutive 16 bytes.
-    // Element i of lane (g, rr) in tile (nt, mt) is weight row
-    // 32 nt + 8 (i / 4) + 4 g + i % 4 and token 32 mt + rr. ----
-    // bytes per staged row, padded by 16 where two wavefronts' rows still
-    // fit one buffer (fewer bank conflicts on the row writes)
-    constexpr int kRow = 2 * 64 * (BN * 2 + 16) <= SM::kBuf ? BN * 2 + 16 : BN * 2;
-    static_assert(2 * 64 * kRow <= SM::kBuf, "two wavefronts' rows fit one buffer");
-    uint8_t *stage = (wave < 2 ? lds0 : lds1) + (wave % 2) * 64 * kRow;
+    // ---- epilogue, straight from registers: element i of lane (g, rr) in
+    // tile (nt, mt) is weight row 32 nt + 8 (i / 4) + 4 g + i % 4 and token
+    // 32 mt + rr, so for a = i / 4 a lane holds 4 consecutive outputs of its
+    // token row and lane rr + 32 the next 4.  Bias is added in fp32 and each
+    // pair rounded to bf16 once (v_cvt_pk_bf16_f32); then v_permlane32_swap
+    // trades the a = 1 (3) quarter of lanes 0..31 for the a = 0 (2) quarter of
+    // lanes 32..63, and every lane stores 8 consecutive outputs (16 bytes):
+    // lanes 0..31 those of a = 0 (2), lanes 32..63 those of a = 1 (3). ----
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    auto pk = [](float lo, float hi) -> uint32_t {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+    };
+    auto epilogue = [&](auto biasconst) {
+        constexpr bool kBias = decltype(biasconst)::value;
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt)
+        for (int nt = 0; nt < NTW; ++nt) {
+            v2u bias2[4];                                 // packed bf16 pairs
+            if constexpr (kBias) {
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-            const int nl = 32 * nt + 8 * a + 4 * g;
-            float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (p.bias && n0 + nl < p.N)
-                for (int i = 0; i < 4; ++i) bv[i] = bf16_to_f32(p.bias[n0 + nl + i]);
+                for (int a = 0; a < 4; ++a)
+                    bias2[a] = *reinterpret_cast<const v2u *>(bias_lds + 32 * nt + 8 * a + 4 * g);
+            }
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 const v16f &c = acc[nt][mt];
-                v2u o = {bf16_bits(c[4 * a] + bv[0]) | (bf16_bits(c[4 * a + 1] + bv[1]) << 16),
-                         bf16_bits(c[4 * a + 2] + bv[2]) | (bf16_bits(c[4 * a + 3] + bv[3]) << 16)};
-                *reinterpret_cast<v2u *>(stage + (32 * mt + rr) * kRow + 2 * nl) = o;
+                const int64_t m = m0 + 64 * wave + 32 * mt + rr;
+#pragma unroll
+                for (int a0 = 0; a0 < 4; a0 += 2) {
+                    uint32_t o[2][2];                     // [a - a0][dword]
+#pragma unroll
+                    for (int d = 0; d < 2; ++d)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const int i = 4 * (a0 + d) + 2 * h;
+                            float lo = c[i], hi = c[i + 1];
+                            if constexpr (kBias) {
+                                const uint32_t bb = bias2[a0 + d][h];
+                                lo += bf16_to_f32(bb & 0xFFFFu);
+                                hi += bf16_to_f32(bb >> 16);
+                            }
+                            o[d][h] = pk(lo, hi);
+                        }
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const auto sw = __builtin_amdgcn_permlane32_swap(o[0][h], o[1][h], false,
+                                                                         false);
+                        o[0][h] = sw[0];
+                        o[1][h] = sw[1];
+                    }
+                    const int64_t n = n0 + 32 * nt + 8 * (a0 + g);
+                    if (m < p.M && n < p.N)
+                        *reinterpret_cast<v4u *>(p.y + m * p.ldy + n) =
+                            v4u{o[0][0], o[0][1], o[1][0], o[1][1]};
+                }
             }
+            // one tile at a time: reading every accumulator up front would
+            // take more registers than the loop leaves
+            __builtin_amdgcn_sched_barrier(0);
         }
-    constexpr int kChunks = BN * 2 / 16;                  // 16-byte pieces per row
-#pragma unroll 4
-    for (int c = lane; c < 64 * kChunks; c += 64) {
-        const int row = c / kChunks, piece = c % kChunks;
-        const int64_t m = m0 + 64 * wave + row, n = n0 + 8 * piece;
-        const v4u v = *reinterpret_cast<const v4u *>(stage + row * kRow + 16 * piece);
-        if (m < p.M && n < p.N) *reinterpret_cast<v4u *>(p.y + m * p.ldy + n) = v;
-    }
+    };
+    if (p.bias)
+        epilogue(std::true_type{});
+    else
+        epilogue(std::false_type{});
 }
 
 template <int LAYOUT, int NTW>
