@@ -209,8 +209,8 @@ mx_status mx_linear_workspace(int elem, int layout, int64_t N, int64_t K, int64_
         *bytes = (size_t)(round256(mx::act_t16_data_bytes(M, K)) + mx::act_codes_t16_bytes(M, K));
     else if (act == ACT_MXFP8 && !prequantized)         // row-major, chunked GEMV for long K
         *bytes = (size_t)(round256(M * padded_k(K)) + round256(M * (padded_k(K) / 32)));
-    else if (act == ACT_MXFP8 && M > kGemvMaxM)         // row-major codes restaged for the GEMM
-        *bytes = (size_t)mx::act_codes_t16_bytes(M, K);
+    else if (act == ACT_MXFP8 && M > kGemvMaxM)         // row-major input restaged into T16
+        *bytes = (size_t)(round256(mx::act_t16_data_bytes(M, K)) + mx::act_codes_t16_bytes(M, K));
     return MX_OK;
 }
 
@@ -290,14 +290,14 @@ mx_status mx_linear(int elem, int layout, int64_t N, int64_t K, const void *w_pa
         g.K = K;
         g.M = M;
         g.xq = aq;
-        g.ldq = lq;
-        g.xt16 = a16;
         g.xct = ac;
         if (!a16) {
-            // restage the row-major codes into the T16 code layout
-            if ((st = launched(mx::launch_act_codes_t16(M, K, ac, lc, wsp, s))) != MX_OK)
-                return st;
-            g.xct = wsp;
+            // restage the row-major bytes and codes into the T16 layout
+            uint8_t *q = wsp, *c = wsp + round256(mx::act_t16_data_bytes(M, K));
+            if ((st = launched(mx::launch_act_data_t16(M, K, aq, lq, q, s))) != MX_OK) return st;
+            if ((st = launched(mx::launch_act_codes_t16(M, K, ac, lc, c, s))) != MX_OK) return st;
+            g.xq = q;
+            g.xct = c;
         }
         g.bias = static_cast<const uint16_t *>(bias);
         g.y = static_cast<uint16_t *>(y);

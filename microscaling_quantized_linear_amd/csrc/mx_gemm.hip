@@ -2,7 +2,7 @@
 //
 // ([rocm_native] module notes and apply_weights: fp8 e4m3 weights with E8M0
 // block scales consumed directly by the CDNA4 microscaling matrix cores,
-// activations quantized per token with row-major codes.)
+// activations quantized per token.)
 //
 // Workgroup tile: BN weight rows x 256 tokens, 4 wavefronts side by side
 // along the tokens: each wavefront owns all BN rows and 64 tokens, NTW x 2
@@ -10,16 +10,21 @@
 // (A = weights, B = activations, both with per-lane E8M0 scales).  On
 // MI355X the 32 x 32 x 64 form issues at its full rate (64 cycles for 2^17
 // flop); the 16 x 16 x 128 form measured about 41 cycles for half as many.
-// Per 128-K step the workgroup copies its weight chunks (W-T16, 2 KB per 16
-// rows) and its activation rows (already in fragment order when they come in
-// the T16 layout, else rearranged into it by the copy's addressing) straight
-// from memory into one of two LDS buffers (buffer loads with an LDS
-// destination) while the matrix cores work on the other; one barrier per
-// step.  A 32 x 32 x 64 operand lane (row r, K group g) reads its two
-// 16-byte pieces from those 16-row chunks.  Scale codes are read once per
-// four steps as dwords whose byte u is step 4q + u's code, picked by the
-// MFMA's byte select.  Out-of-range rows and K tails read zeros through
-// buffer-resource bounds.
+//
+// Operands, per 128-K step:
+//  - weights (shared by the four wavefronts): the workgroup copies the
+//    step's W-T16 chunks (2 KB per 16 rows) straight from memory into one of
+//    two LDS buffers (buffer loads with an LDS destination) while the matrix
+//    cores work on the other; one barrier per step.  A 32 x 32 x 64 operand
+//    lane (row r, K group g) reads its two 16-byte pieces from those chunks.
+//  - activations (private to a wavefront): read from the T16 layout straight
+//    into registers, one step ahead, two register sets.  Keeping them out of
+//    LDS leaves the weights as LDS's only traffic (about two thirds of it
+//    before), and no wavefront waits on LDS for its activations after the
+//    barrier.
+// Scale codes are read once per four steps as dwords whose byte u is step
+// 4 q + u's code, picked by the MFMA's byte select.  Out-of-range rows, tokens
+// and K tails read zeros through buffer-resource bounds.
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -29,36 +34,23 @@ namespace mx {
 
 constexpr int kBM = 256;           // tokens per workgroup
 
-// Per LDS buffer: the step's weight chunks (2 NTW x 2 KB, W-T16 as stored) then
-// the activation tile in MFMA fragment order (16 chunks of 16 rows x 128 K:
-// byte 1024 h + 16 l of chunk mt holds row 16 mt + l%16, K 64 h + 16 (l/16)).
-template <int NTW>
-struct GemmSmem {
-    static constexpr int kWBytes = 2 * NTW * 2048;
-    static constexpr int kXBytes = kBM / 16 * 2048;
-    static constexpr int kBuf = kWBytes + kXBytes;
-    static constexpr int kDma = kBuf / 1024;              // 1 KB DMA loads per step
-};
-
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int LAYOUT, int NTW>
 __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
-    using SM = GemmSmem<NTW>;
-    // two distinct buffers: the compiler can then tell the DMA into one from
-    // the operand reads of the other and waits only where it must
-    __shared__ __attribute__((aligned(1024))) uint8_t lds0[SM::kBuf];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds1[SM::kBuf];
     constexpr int BN = NTW * 32;
+    constexpr int kWBytes = 2 * NTW * 2048;               // one step's weight chunks
+    // two distinct buffers: the compiler can then tell the copies into one
+    // from the operand reads of the other and waits only where it must
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[kWBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[kWBytes];
     static_assert(BN <= 256, "one bias value per thread");
     __shared__ __attribute__((aligned(16))) uint16_t bias_lds[BN];
     const int tid = threadIdx.x, lane = tid % 64;
     // bounded so the compiler can tell the two LDS buffers' accesses apart
-    // (otherwise it waits for the next step's copies before reading this one)
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64) & 3;
-    const int r = lane % 16, j = lane / 16;
-    const int64_t Kp = (p.K + 127) / 128 * 128, S = Kp / 128, T = p.N / 16, Q = (S + 3) / 4;
-    const int64_t KB = p.K / 32;
+    const int S = (int)((p.K + 127) / 128), Q = (S + 3) / 4;
+    const int64_t T = p.N / 16, MB = (p.M + 15) / 16;
 
     // tile order: consecutive workgroups go to different XCDs; give each XCD
     // a band of N tiles so the weight panels it streams stay in its L2
@@ -74,178 +66,164 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     }
     const int64_t n0 = tn * BN, m0 = tm * kBM;
     const int64_t t0 = n0 / 16;                           // first weight tile
+    const int64_t mbw = m0 / 16 + 4 * wave;               // this wavefront's first token tile
 
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w, (uint32_t)(T * S * 2048));
-    const int64_t MB = (p.M + 15) / 16;
-    const __amdgpu_buffer_rsrc_t xr =
-        make_rsrc(p.xq, p.xt16 ? (uint32_t)(MB * S * 2048) : (uint32_t)(p.M * p.ldq));
+    const __amdgpu_buffer_rsrc_t wr =
+        make_rsrc(p.w + t0 * S * 2048, (uint32_t)((T - t0) * S * 2048));
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.xq, (uint32_t)(MB * S * 2048));
     const __amdgpu_buffer_rsrc_t xcr = make_rsrc(p.xct, (uint32_t)act_codes_t16_bytes(p.M, p.K));
     const __amdgpu_buffer_rsrc_t cr =
         make_rsrc(p.codes, LAYOUT == ROW32 ? (uint32_t)(T * Q * 256)
                                            : (uint32_t)((p.N / 32) * Q * 16));
 
-    // ---- DMA assignment: wave w issues weight chunk-halves w, w + 4, ... and
-    // activation chunk-halves w, w + 4, ...; chunk-half i lands at i KB.
-    // Offsets of out-of-range loads get bit 31 set (every resource is below
-    // 2 GiB, so those lanes read zeros); no branches in the loop body.
-    constexpr int kWq = NTW;                              // 4 NTW weight loads / 4 waves
-    constexpr int kXq = 8;                                // 32 activation loads / 4 waves
-    uint32_t wbase[kWq], xbase[kXq], xkmax[kXq];
+    // ---- weight copies: wavefront w copies chunk-halves w, w + 4, ... of
+    // the step (NTW of them); chunk-half i = 2 c + h lands at i KB.  Offsets
+    // of out-of-range loads get bit 31 set (every resource is below 2 GiB, so
+    // those lanes read zeros); no branches in the loop body.
+    uint32_t wofs[NTW];
 #pragma unroll
-    for (int q = 0; q < kWq; ++q) {
-        const int i = wave + 4 * q, c = i / 2, h = i % 2;
-        const int64_t t = t0 + c;
-        wbase[q] = t < T ? (uint32_t)(t * S * 2048 + 1024 * h + 16 * lane) : kOOB;
+    for (int i = 0; i < NTW; ++i) {
+        const int idx = wave + 4 * i, c = idx / 2, h = idx % 2;
+        wofs[i] = t0 + c < T ? (uint32_t)(c * S * 2048 + 1024 * h + 16 * lane) : kOOB;
     }
-#pragma unroll
-    for (int q = 0; q < kXq; ++q) {
-        // wavefront w copies its own 64 tokens: chunks 4 w .. 4 w + 3, both
-        // halves (chunk-half 8 w + q), so it may read them without a barrier
-        const int i = 8 * wave + q, mc = i / 2, h = i % 2;
-        const int64_t row = m0 + 16 * mc + r, k = 64 * h + 16 * j;
-        if (p.xt16) {
-            // T16: the 1 KB block (16-token tile, step, half) is already in
-            // fragment order; padding bytes are zeros
-            const int64_t mb = (m0 + 16 * mc) / 16;
-            xbase[q] = mb < MB ? (uint32_t)(mb * S * 2048 + h * 1024 + 16 * lane) : kOOB;
-            xkmax[q] = (uint32_t)S;
-        } else {
-            xbase[q] = row < p.M ? (uint32_t)(row * p.ldq + k) : kOOB;
-            xkmax[q] = (uint32_t)((p.K - k + 127) / 128);     // steps with 128 s + k < K
-        }
-    }
-    const uint32_t xstep = p.xt16 ? 2048u : 128u;         // bytes per 128-K step
-    // copy i of step s into buf: i < kWq weight chunk-halves, then activation ones
-    constexpr int kCopies = kWq + kXq;
-    auto dma_one = [&](uint8_t *buf, int64_t s, int i) {
-        const uint32_t su = (uint32_t)s;
-        if (i < kWq) {
-            const uint32_t past = su >= (uint32_t)S ? kOOB : 0u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                wr, (lds_void *)(buf + (wave + 4 * i) * 1024), 16,
-                (int)((wbase[i] + su * 2048u) | past), 0, 0, 0);
-        } else {
-            const int q = i - kWq;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xr, (lds_void *)(buf + SM::kWBytes + (8 * wave + q) * 1024), 16,
-                (int)((xbase[q] + su * xstep) | (su >= xkmax[q] ? kOOB : 0u)), 0, 0, 0);
-        }
-    };
-    auto dma = [&](uint8_t *buf, int64_t s) {
-#pragma unroll
-        for (int i = 0; i < kCopies; ++i) dma_one(buf, s, i);
+    auto dma_one = [&](uint8_t *buf, int s, int i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wr, (lds_void *)(buf + (wave + 4 * i) * 1024), 16,
+            (int)((wofs[i] + (uint32_t)s * 2048u) | (s >= S ? kOOB : 0u)), 0, 0, 0);
     };
 
     // ---- 32 x 32 x 64 operands: lane (g, rr) = lane / 32, lane % 32 holds
-    // row rr with K 16 g .. and 32 + 16 g .. of a 64-K half-step kh; in the
-    // 16-row chunks that is chunk 2 T + rr / 16, bytes 1024 kh + 256 g +
+    // row (or token) rr with K 16 g .. and 32 + 16 g .. of a 64-K half-step
+    // kh; in a 16-row chunk that is chunk rr / 16, bytes 1024 kh + 256 g +
     // 16 (rr % 16) and 512 further ----
     const int rr = lane % 32, g = lane / 32;
     const int off_lane = (rr / 16) * 2048 + 256 * g + 16 * (rr % 16);
+    auto rd = [&](const uint8_t *base, int kh) -> v8i {
+        const uint8_t *cp = base + off_lane + 1024 * kh;
+        return cat8(*reinterpret_cast<const v4u *>(cp), *reinterpret_cast<const v4u *>(cp + 512));
+    };
+
+    // ---- activation fragments, straight from the T16 layout: token slab mt
+    // (32 tokens) of this wavefront is token tiles mbw + 2 mt and + 1 ----
+    // (every out-of-range case is folded in with bit 31, without branches:
+    // a branch would split the step's basic block, and with it the order the
+    // scheduling barriers keep)
+    const uint32_t xlane = (uint32_t)((rr / 16) * S * 2048 + 256 * g + 16 * (rr % 16));
+    uint32_t xtile[2];                                    // slab mt's first tile, or kOOB
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+        xtile[mt] = mbw + 2 * mt < MB ? (uint32_t)((mbw + 2 * mt) * S * 2048) : kOOB;
+    typedef v8i BFrag[2][2];                              // [kh][mt]
+    auto load_b_one = [&](BFrag &b, int s, int n) {       // load n of 8: (mt, kh, piece)
+        const int mt = n / 4, kh = (n / 2) % 2, pc = n % 2;
+        const uint32_t u = (xtile[mt] + (uint32_t)s * 2048u) | (s >= S ? kOOB : 0u);
+        const v4u v = load16(xr, (xlane + u + 1024u * kh + 512u * pc) | (u & kOOB));
+        if (pc == 0) {
+            b[kh][mt][0] = (int)v[0]; b[kh][mt][1] = (int)v[1];
+            b[kh][mt][2] = (int)v[2]; b[kh][mt][3] = (int)v[3];
+        } else {
+            b[kh][mt][4] = (int)v[0]; b[kh][mt][5] = (int)v[1];
+            b[kh][mt][6] = (int)v[2]; b[kh][mt][7] = (int)v[3];
+        }
+    };
 
     // ---- per-lane scale dwords of one quad of four steps: byte u of each
     // dword is step 4 q + u's code, picked by the MFMA's opsel; lane (g, rr)
-    // of half-step kh needs block 2 kh + g of its row ----
+    // of half-step kh needs block 2 kh + g of its row.  In the 16-row C-T16
+    // code layout (weights with ROW32, and the activations) that is dword
+    // 16 (2 kh + g) + rr % 16 of tile row / 16; BLK32 keeps one dword per
+    // (32-row group, block). ----
     struct QScales {
         uint32_t w[NTW][2], x[2][2];
     };
-    uint32_t cwbase[NTW][2], cxbase[2][2];
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt)
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            const int jb = 2 * kh + g;                    // block of the 128-K step
-            const int64_t row = n0 + 32 * nt + rr;
-            if (LAYOUT == ROW32)
-                cwbase[nt][kh] = row < p.N ? (uint32_t)((row / 16) * Q * 256 +
-                                                        4 * (16 * jb + row % 16)) : kOOB;
-            else
-                cwbase[nt][kh] = row < p.N ? (uint32_t)((row / 32) * Q * 16 + 4 * jb) : kOOB;
-        }
+    const uint32_t clane = (uint32_t)((rr / 16) * Q * 256 + 64 * g + 4 * (rr % 16));
+    uint32_t xctile[2];                                   // slab mt's first code tile, or kOOB
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            const int jb = 2 * kh + g;
-            const int64_t tok = m0 + 64 * wave + 32 * mt + rr;    // T16 code layout
-            cxbase[mt][kh] = tok < 16 * MB ? (uint32_t)((tok / 16) * Q * 256 +
-                                                         4 * (16 * jb + tok % 16)) : kOOB;
-        }
-    auto load_qscales = [&](int64_t q, QScales &out) {
-        const uint32_t qu = (uint32_t)q, past = qu >= (uint32_t)Q ? kOOB : 0u;
+        xctile[mt] = mbw + 2 * mt < MB ? (uint32_t)((mbw + 2 * mt) * Q * 256) : kOOB;
+    auto load_qscales = [&](int q, QScales &out) {
+        // rows past N and tokens past the last tile fall outside the
+        // resources; quads past Q get bit 31
+        const uint32_t past = q >= Q ? kOOB : 0u;
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-                out.w[nt][kh] = load4(cr, (cwbase[nt][kh] + qu * (LAYOUT == ROW32 ? 256u : 16u)) | past);
+            for (int kh = 0; kh < 2; ++kh) {
+                uint32_t off;
+                if (LAYOUT == ROW32)
+                    off = clane + (uint32_t)(((n0 / 16 + 2 * nt) * Q + q) * 256 + 128 * kh);
+                else
+                    off = 4u * g + (uint32_t)(((n0 / 32 + nt) * Q + q) * 16 + 8 * kh);
+                out.w[nt][kh] = load4(cr, off | past);
+            }
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-                out.x[mt][kh] = load4(xcr, (cxbase[mt][kh] + qu * 256u) | past);
+            for (int kh = 0; kh < 2; ++kh) {
+                const uint32_t u = xctile[mt] + (uint32_t)q * 256u + 128u * kh;
+                out.x[mt][kh] = load4(xcr, (clane + u) | (u & kOOB) | past);
+            }
     };
 
     typedef float v16f __attribute__((ext_vector_type(16)));
     // first written by the first step's MFMAs, which take a zero C operand
     v16f acc[NTW][2];
 
-    // one 128-K step, step u of its quad: the MFMAs of step s from `cur` with
-    // the quad's scales `sc`, interleaved with the copies of step s + 1 into
-    // `nxt`.  The 2 NTW
-    // MFMA groups (half-step kh, weight tile nt) each take two MFMAs; a
-    // group's weight fragment is read two groups ahead, the activation
-    // fragments of a half-step with the reads of its first groups.
-    auto rd = [&](const uint8_t *base, int kh) -> v8i {
-        const uint8_t *cp = base + off_lane + 1024 * kh;
-        return cat8(*reinterpret_cast<const v4u *>(cp), *reinterpret_cast<const v4u *>(cp + 512));
+    // The barrier that ends a step orders LDS only through the copies'
+    // completion: each wavefront has waited for its own copies into `nxt`
+    // (vmcnt) and has consumed every operand read from `cur` (its MFMAs are
+    // issued), so a plain s_barrier suffices; the empty asm statements keep
+    // the compiler from moving any memory access across it.
+    auto step_barrier = [] {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
     };
-    // the wavefront's activation fragments of one step (both half-steps);
-    // this wavefront alone copies them, so they are read as soon as its own
-    // copies have landed, before the barrier
-    v8i bf[2][2];
-    auto read_b = [&](const uint8_t *buf) {
-        const uint8_t *xb = buf + SM::kWBytes + (4 * wave) * 2048;
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) bf[kh][mt] = rd(xb + 2 * mt * 2048, kh);
-    };
-    auto step = [&](uint8_t *cur, uint8_t *nxt, int64_t s, const QScales &sc, auto uconst,
-                    auto firstconst) {
+    // One 128-K step, step u of its quad: the MFMAs of step s from `cur` and
+    // the activation fragments `bc`, with the quad's scales `sc`.  Spread over
+    // its 2 NTW MFMA groups (half-step kh, weight tile nt; two MFMAs each) go
+    // out, two per group, first the weight copies of step s + 1 into `nxt`,
+    // then the eight activation loads of step s + 1 into `bn`; a group's
+    // weight fragment is read two groups ahead.  Issued all at once, the
+    // copies would queue on the CU's address path and hold back the MFMAs.
+    constexpr int kMem = NTW + 8;                         // memory ops per step
+    static_assert(kMem <= 4 * NTW, "two per group in the first half of the step");
+    auto step = [&](uint8_t *cur, uint8_t *nxt, int s, const QScales &sc, BFrag &bc, BFrag &bn,
+                    auto uconst, auto firstconst) {
         constexpr int U = decltype(uconst)::value;
         constexpr bool kFirst = decltype(firstconst)::value;
-        const uint8_t *wb = cur;
         constexpr int NG = 2 * NTW;                       // groups (kh, nt), kh major
         v8i af[3];
         auto issue = [&](int k) {                         // group k's weight fragment
-            af[k % 3] = rd(wb + 2 * (k % NTW) * 2048, k / NTW);
+            af[k % 3] = rd(cur + 2 * (k % NTW) * 2048, k / NTW);
         };
         issue(0);
         issue(1);
-        // the copies of step s + 1 go out two per MFMA group from the top of
-        // the step: issued all at once, the four wavefronts' 60 KB queue on
-        // the CU's address path (64 B/clock) and hold back the MFMAs; spread,
-        // the copies and the matrix cores overlap and the last copy still has
-        // half a step to land before the barrier
+        __builtin_amdgcn_sched_barrier(0);               // the reads go out first
 #pragma unroll
         for (int k = 0; k < NG; ++k) {
-            if (2 * k < kCopies) dma_one(nxt, s + 1, 2 * k);
-            if (2 * k + 1 < kCopies) dma_one(nxt, s + 1, 2 * k + 1);
+#pragma unroll
+            for (int e = 2 * k; e < 2 * k + 2; ++e) {
+                if (e < NTW) dma_one(nxt, s + 1, e);
+                else if (e < kMem) load_b_one(bn, s + 1, e - NTW);
+            }
             if (k + 2 < NG) issue(k + 2);
             __builtin_amdgcn_sched_barrier(0);
             const int kh = k / NTW, nt = k % NTW;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
                 acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    af[k % 3], bf[kh][mt], kFirst && kh == 0 ? v16f{} : acc[nt][mt], 0, 0, U,
+                    af[k % 3], bc[kh][mt], kFirst && kh == 0 ? v16f{} : acc[nt][mt], 0, 0, U,
                     (int)sc.w[nt][kh], U, (int)sc.x[mt][kh]);
             __builtin_amdgcn_sched_barrier(0);
         }
         // this wavefront's copies of step s + 1 have landed before any
-        // wavefront reads them
-        __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
-        read_b(nxt);
-        __syncthreads();
+        // wavefront reads them (the eight activation loads issued after them
+        // may still be in flight: they are this wavefront's own registers)
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(8));
+        step_barrier();
     };
     using U0 = std::integral_constant<int, 0>;
     using U1 = std::integral_constant<int, 1>;
@@ -258,29 +236,32 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     if (p.bias && tid < BN) bias_lds[tid] = n0 + tid < p.N ? p.bias[n0 + tid] : 0;
 
     QScales qa, qb;
-    dma(lds0, 0);
+    BFrag ba, bb;
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) dma_one(lds0, 0, i);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) load_b_one(ba, 0, n);
     load_qscales(0, qa);
     __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
     __syncthreads();
-    read_b(lds0);
-    // eight steps (two quads) per iteration: each LDS buffer is a fixed object
-    // and the two scale sets alternate without copies; a step at or past S
-    // reads zeros and adds nothing
-    for (int64_t s = 0; s < S; s += 8) {
-        const int64_t q = s / 4;
+    // eight steps (two quads) per iteration: each LDS buffer and activation
+    // register set is a fixed object and the two scale sets alternate without
+    // copies; a step at or past S reads zeros and adds nothing
+    for (int s = 0; s < S; s += 8) {
+        const int q = s / 4;
         load_qscales(q + 1, qb);
         if (s == 0)
-            step(lds0, lds1, s + 0, qa, U0{}, std::true_type{});
+            step(lds0, lds1, s + 0, qa, ba, bb, U0{}, std::true_type{});
         else
-            step(lds0, lds1, s + 0, qa, U0{}, F0{});
-        step(lds1, lds0, s + 1, qa, U1{}, F0{});
-        step(lds0, lds1, s + 2, qa, U2{}, F0{});
-        step(lds1, lds0, s + 3, qa, U3{}, F0{});
+            step(lds0, lds1, s + 0, qa, ba, bb, U0{}, F0{});
+        step(lds1, lds0, s + 1, qa, bb, ba, U1{}, F0{});
+        step(lds0, lds1, s + 2, qa, ba, bb, U2{}, F0{});
+        step(lds1, lds0, s + 3, qa, bb, ba, U3{}, F0{});
         load_qscales(q + 2, qa);
-        step(lds0, lds1, s + 4, qb, U0{}, F0{});
-        step(lds1, lds0, s + 5, qb, U1{}, F0{});
-        step(lds0, lds1, s + 6, qb, U2{}, F0{});
-        step(lds1, lds0, s + 7, qb, U3{}, F0{});
+        step(lds0, lds1, s + 4, qb, ba, bb, U0{}, F0{});
+        step(lds1, lds0, s + 5, qb, bb, ba, U1{}, F0{});
+        step(lds0, lds1, s + 6, qb, ba, bb, U2{}, F0{});
+        step(lds1, lds0, s + 7, qb, bb, ba, U3{}, F0{});
     }
 
     // ---- epilogue, straight from registers: element i of lane (g, rr) in

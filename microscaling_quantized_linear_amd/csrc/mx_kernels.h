@@ -36,9 +36,7 @@ struct GemvArgs {
 struct GemmArgs {
     const uint8_t *w, *codes;
     int64_t N, K, M;
-    const uint8_t *xq;       // row-major [M, ldq], or the T16 layout when xt16
-    int64_t ldq;
-    bool xt16;
+    const uint8_t *xq;       // activation bytes in the T16 data layout
     const uint8_t *xct;      // activation codes in the T16 code layout
     const uint16_t *bias;
     uint16_t *y;
@@ -52,6 +50,9 @@ __host__ __device__ inline int64_t act_codes_t16_bytes(int64_t M, int64_t K) {
 }
 hipError_t launch_act_codes_t16(int64_t M, int64_t K, const void *xc, int64_t ldc, void *out,
                                 hipStream_t stream);
+// row-major e4m3 activations [M, ldq] restaged into the T16 data layout
+hipError_t launch_act_data_t16(int64_t M, int64_t K, const void *xq, int64_t ldq, void *out,
+                               hipStream_t stream);
 
 hipError_t launch_pack(int elem, int layout, int64_t E, int64_t N, int64_t K, const void *w,
                        const void *codes, void *wp, void *cp, int *bad, hipStream_t stream);

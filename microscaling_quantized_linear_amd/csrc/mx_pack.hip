@@ -117,6 +117,32 @@ hipError_t launch_act_codes_t16(int64_t M, int64_t K, const void *xc, int64_t ld
     return hipGetLastError();
 }
 
+// Row-major e4m3 activations [M, ldq] -> the T16 data layout: 2,048 bytes
+// per (16-token tile mb, 128-K step s); byte 1024 h + 16 l + c (l = 16 j + r)
+// holds xq[16 mb + r][128 s + 64 h + 16 j + c].  One thread per 16-byte
+// piece; tokens past M and K past the end read as zeros (K is a multiple of
+// 32, so a piece is wholly inside or outside).
+__global__ void __launch_bounds__(256) act_data_t16_kernel(int64_t M, int64_t K,
+                                                           const uint8_t *__restrict__ xq,
+                                                           int64_t ldq, v4u *__restrict__ out,
+                                                           int64_t npieces) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= npieces) return;
+    const int64_t S = (K + 127) / 128;
+    const int64_t l = p % 64, blk = p / 64, h = blk % 2, ms = blk / 2, s = ms % S, mb = ms / S;
+    const int64_t row = 16 * mb + l % 16, k = 128 * s + 64 * h + 16 * (l / 16);
+    out[p] = (row < M && k < K) ? *reinterpret_cast<const v4u *>(xq + row * ldq + k)
+                                : v4u{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_act_data_t16(int64_t M, int64_t K, const void *xq, int64_t ldq, void *out,
+                               hipStream_t stream) {
+    const int64_t npieces = act_t16_data_bytes(M, K) / 16;
+    hipLaunchKernelGGL(act_data_t16_kernel, dim3((unsigned)((npieces + 255) / 256)), dim3(256), 0,
+                       stream, M, K, (const uint8_t *)xq, ldq, (v4u *)out, npieces);
+    return hipGetLastError();
+}
+
 hipError_t launch_pack(int elem, int layout, int64_t E, int64_t N, int64_t K, const void *w,
                        const void *codes, void *wp, void *cp, int *bad, hipStream_t stream) {
     const int64_t Kp = (K + 127) / 128 * 128, S = Kp / 128, Q = (S + 3) / 4;

@@ -161,6 +161,10 @@ def test_gemm_small(g, layout, M, N, K):
     ref = oracle.linear(E4M3, layout, N, K, w, codes, M, MXFP8, xq=oq, xcodes=oc, bias=b)
     y = g.linear(E4M3, layout, N, K, wp, cp, MXFP8, x=x, rule=OCP, bias=b)
     g.assert_close(y, ref, "gemm")
+    # row-major pre-quantized input (restaged into the tile-major layout in
+    # the workspace) gives the same bits
+    y2 = g.linear(E4M3, layout, N, K, wp, cp, MXFP8, xq=oq, xcodes=oc, bias=b)
+    assert np.array_equal(y, y2)
 
 
 def test_extreme_codes_w8a8(g):
