@@ -153,8 +153,11 @@ mx_status mx_quant_act_t16(int64_t M, int64_t K, const void *x, int64_t ldx, voi
  *   act == MX_ACT_MXFP8 quantized inside the call (prequantized = 0): the
  *     T16 activation, round256(MB * S * 2048) + MB * Q * 256;
  *   act == MX_ACT_MXFP8 pre-quantized row-major with M > 64 (prefill GEMM):
- *     MB * Q * 256 for the codes restaged into the T16 code layout;
- *   otherwise 0 (MX_ACT_BF16, MX_ACT_MXFP8_T16, or pre-quantized M <= 64). */
+ *     the same size: the GEMM reads the T16 layout, so the bytes and codes
+ *     are restaged into it;
+ *   otherwise 0 (MX_ACT_BF16, MX_ACT_MXFP8_T16, or pre-quantized M <= 64).
+ * (K > 8192 with M <= 64 quantized inside the call is the exception: the
+ * row-major staging round256(M * Kp) + round256(M * Kp / 32).) */
 mx_status mx_linear_workspace(int elem, int layout, int64_t N, int64_t K,
                               int64_t M, int act, int prequantized,
                               size_t *bytes);
