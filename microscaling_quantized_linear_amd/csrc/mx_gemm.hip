@@ -14,14 +14,17 @@
 // Operands, per 128-K step:
 //  - weights (shared by the four wavefronts): the workgroup copies the
 //    step's W-T16 chunks (2 KB per 16 rows) straight from memory into one of
-//    two LDS buffers (buffer loads with an LDS destination) while the matrix
-//    cores work on the other; one barrier per step.  A 32 x 32 x 64 operand
-//    lane (row r, K group g) reads its two 16-byte pieces from those chunks.
+//    four LDS buffers (buffer loads with an LDS destination), two steps ahead
+//    of the matrix cores; one barrier per step.  A 32 x 32 x 64 operand lane
+//    (row r, K group g) reads its two 16-byte pieces from those chunks.
 //  - activations (private to a wavefront): read from the T16 layout straight
-//    into registers, one step ahead, two register sets.  Keeping them out of
-//    LDS leaves the weights as LDS's only traffic (about two thirds of it
-//    before), and no wavefront waits on LDS for its activations after the
-//    barrier.
+//    into registers at the top of the step before they are needed, two
+//    register sets.  Keeping them out of LDS leaves the weights as LDS's only
+//    traffic (about two thirds of it before), and no wavefront waits on LDS
+//    for its activations after the barrier.
+// Measured on MI355X, the first reader of a K slice often misses the XCD's
+// L2 (each XCD works on some 20 MB of panels at once), so loads get more
+// than a step of lead.
 // Scale codes are read once per four steps as dwords whose byte u is step
 // 4 q + u's code, picked by the MFMA's byte select.  Out-of-range rows, tokens
 // and K tails read zeros through buffer-resource bounds.
@@ -40,10 +43,12 @@ template <int LAYOUT, int NTW>
 __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     constexpr int BN = NTW * 32;
     constexpr int kWBytes = 2 * NTW * 2048;               // one step's weight chunks
-    // two distinct buffers: the compiler can then tell the copies into one
-    // from the operand reads of the other and waits only where it must
+    // four distinct buffers: the compiler can then tell the copies into one
+    // from the operand reads of another and waits only where it must
     __shared__ __attribute__((aligned(1024))) uint8_t lds0[kWBytes];
     __shared__ __attribute__((aligned(1024))) uint8_t lds1[kWBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[kWBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds3[kWBytes];
     static_assert(BN <= 256, "one bias value per thread");
     __shared__ __attribute__((aligned(16))) uint16_t bias_lds[BN];
     const int tid = threadIdx.x, lane = tid % 64;
@@ -114,8 +119,8 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     for (int mt = 0; mt < 2; ++mt)
         xtile[mt] = mbw + 2 * mt < MB ? (uint32_t)((mbw + 2 * mt) * S * 2048) : kOOB;
     typedef v8i BFrag[2][2];                              // [kh][mt]
-    auto load_b_one = [&](BFrag &b, int s, int n) {       // load n of 8: (mt, kh, piece)
-        const int mt = n / 4, kh = (n / 2) % 2, pc = n % 2;
+    auto load_b_one = [&](BFrag &b, int s, int n) {       // load n of 8: (kh, mt, piece)
+        const int kh = n / 4, mt = (n / 2) % 2, pc = n % 2;   // the first groups' half first
         const uint32_t u = (xtile[mt] + (uint32_t)s * 2048u) | (s >= S ? kOOB : 0u);
         const v4u v = load16(xr, (xlane + u + 1024u * kh + 512u * pc) | (u & kOOB));
         if (pc == 0) {
@@ -169,11 +174,12 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     // first written by the first step's MFMAs, which take a zero C operand
     v16f acc[NTW][2];
 
-    // The barrier that ends a step orders LDS only through the copies'
-    // completion: each wavefront has waited for its own copies into `nxt`
-    // (vmcnt) and has consumed every operand read from `cur` (its MFMAs are
-    // issued), so a plain s_barrier suffices; the empty asm statements keep
-    // the compiler from moving any memory access across it.
+    // The barrier that ends step s orders LDS only through the copies'
+    // completion: each wavefront has waited for its own copies of step s + 1
+    // (vmcnt) and has consumed every operand read from step s's buffer (its
+    // MFMAs are issued; that buffer is refilled two steps later), so a plain
+    // s_barrier suffices; the empty asm statements keep the compiler from
+    // moving any memory access across it.
     auto step_barrier = [] {
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::: "memory");
@@ -184,14 +190,14 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     // One 128-K step, step u of its quad: the MFMAs of step s from `cur` and
     // the activation fragments `bc`, with the quad's scales `sc`.  Spread over
     // its 2 NTW MFMA groups (half-step kh, weight tile nt; two MFMAs each) go
-    // out, two per group, first the weight copies of step s + 1 into `nxt`,
-    // then the eight activation loads of step s + 1 into `bn`; a group's
+    // out, two per group, first the eight activation loads of step s + 1
+    // into `bn`, then the weight copies of step s + 2 into `ahead`; a group's
     // weight fragment is read two groups ahead.  Issued all at once, the
-    // copies would queue on the CU's address path and hold back the MFMAs.
+    // loads would queue on the CU's address path and hold back the MFMAs.
     constexpr int kMem = NTW + 8;                         // memory ops per step
     static_assert(kMem <= 4 * NTW, "two per group in the first half of the step");
-    auto step = [&](uint8_t *cur, uint8_t *nxt, int s, const QScales &sc, BFrag &bc, BFrag &bn,
-                    auto uconst, auto firstconst) {
+    auto step = [&](uint8_t *cur, uint8_t *ahead, int s, const QScales &sc, BFrag &bc,
+                    BFrag &bn, auto uconst, auto firstconst) {
         constexpr int U = decltype(uconst)::value;
         constexpr bool kFirst = decltype(firstconst)::value;
         constexpr int NG = 2 * NTW;                       // groups (kh, nt), kh major
@@ -206,8 +212,8 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
         for (int k = 0; k < NG; ++k) {
 #pragma unroll
             for (int e = 2 * k; e < 2 * k + 2; ++e) {
-                if (e < NTW) dma_one(nxt, s + 1, e);
-                else if (e < kMem) load_b_one(bn, s + 1, e - NTW);
+                if (e < 8) load_b_one(bn, s + 1, e);
+                else if (e < kMem) dma_one(ahead, s + 2, e - 8);
             }
             if (k + 2 < NG) issue(k + 2);
             __builtin_amdgcn_sched_barrier(0);
@@ -219,10 +225,11 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
                     (int)sc.w[nt][kh], U, (int)sc.x[mt][kh]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // this wavefront's copies of step s + 1 have landed before any
-        // wavefront reads them (the eight activation loads issued after them
-        // may still be in flight: they are this wavefront's own registers)
-        __builtin_amdgcn_s_waitcnt(vmcnt_only(8));
+        // this wavefront's copies of step s + 1 (issued during step s - 1)
+        // have landed before any wavefront reads them; this step's kMem loads
+        // may still be in flight
+        static_assert(kMem < 64, "vmcnt holds 6 bits");
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(kMem));
         step_barrier();
     };
     using U0 = std::integral_constant<int, 0>;
@@ -242,7 +249,11 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
 #pragma unroll
     for (int n = 0; n < 8; ++n) load_b_one(ba, 0, n);
     load_qscales(0, qa);
-    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) dma_one(lds1, 1, i);
+    // step 0's copies, activations and scales have landed; step 1's copies
+    // are checked at the end of step 0
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(NTW));
     __syncthreads();
     // eight steps (two quads) per iteration: each LDS buffer and activation
     // register set is a fixed object and the two scale sets alternate without
@@ -251,17 +262,17 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
         const int q = s / 4;
         load_qscales(q + 1, qb);
         if (s == 0)
-            step(lds0, lds1, s + 0, qa, ba, bb, U0{}, std::true_type{});
+            step(lds0, lds2, s + 0, qa, ba, bb, U0{}, std::true_type{});
         else
-            step(lds0, lds1, s + 0, qa, ba, bb, U0{}, F0{});
-        step(lds1, lds0, s + 1, qa, bb, ba, U1{}, F0{});
-        step(lds0, lds1, s + 2, qa, ba, bb, U2{}, F0{});
-        step(lds1, lds0, s + 3, qa, bb, ba, U3{}, F0{});
+            step(lds0, lds2, s + 0, qa, ba, bb, U0{}, F0{});
+        step(lds1, lds3, s + 1, qa, bb, ba, U1{}, F0{});
+        step(lds2, lds0, s + 2, qa, ba, bb, U2{}, F0{});
+        step(lds3, lds1, s + 3, qa, bb, ba, U3{}, F0{});
         load_qscales(q + 2, qa);
-        step(lds0, lds1, s + 4, qb, ba, bb, U0{}, F0{});
-        step(lds1, lds0, s + 5, qb, bb, ba, U1{}, F0{});
-        step(lds0, lds1, s + 6, qb, ba, bb, U2{}, F0{});
-        step(lds1, lds0, s + 7, qb, bb, ba, U3{}, F0{});
+        step(lds0, lds2, s + 4, qb, ba, bb, U0{}, F0{});
+        step(lds1, lds3, s + 5, qb, bb, ba, U1{}, F0{});
+        step(lds2, lds0, s + 6, qb, ba, bb, U2{}, F0{});
+        step(lds3, lds1, s + 7, qb, bb, ba, U3{}, F0{});
     }
 
     // ---- epilogue, straight from registers: element i of lane (g, rr) in
