@@ -174,12 +174,15 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     // first written by the first step's MFMAs, which take a zero C operand
     v16f acc[NTW][2];
 
-    // The barrier that ends step s orders LDS only through the copies'
-    // completion: each wavefront has waited for its own copies of step s + 1
-    // (vmcnt) and has consumed every operand read from step s's buffer (its
-    // MFMAs are issued; that buffer is refilled two steps later), so a plain
+    // One barrier per step, two MFMA groups before its end: each wavefront
+    // has waited for its own copies of step s + 1 (vmcnt), so after it every
+    // wavefront may read step s + 1's buffer; and every wavefront is past
+    // step s - 1, whose buffer is refilled (with step s + 3) only from step s
+    // + 1 on.  LDS is ordered only through the copies' completion, so a plain
     // s_barrier suffices; the empty asm statements keep the compiler from
-    // moving any memory access across it.
+    // moving any memory access across it.  Placed inside the step, the
+    // barrier waits while the previous group's MFMAs run, and the next step
+    // starts with its first weight fragments already in registers.
     auto step_barrier = [] {
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("" ::: "memory");
@@ -190,53 +193,66 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     // One 128-K step, step u of its quad: the MFMAs of step s from `cur` and
     // the activation fragments `bc`, with the quad's scales `sc`.  Spread over
     // its 2 NTW MFMA groups (half-step kh, weight tile nt; two MFMAs each) go
-    // out, two per group, first the eight activation loads of step s + 1
-    // into `bn`, then the weight copies of step s + 2 into `ahead`; a group's
-    // weight fragment is read two groups ahead.  Issued all at once, the
-    // loads would queue on the CU's address path and hold back the MFMAs.
+    // out, about one per group, first the eight activation loads of step s +
+    // 1 into `bn`, then the weight copies of step s + 2 into `ahead`: each
+    // load is 1 KB, 16 clocks of the CU's address path, so four wavefronts'
+    // loads bunched together would stall the MFMAs behind them.  Weight fragments are read two groups ahead, across
+    // the step boundary into `next` (step s + 1's buffer), into a ring of
+    // four: PH = the ring slot of the step's group 0 (NG = 14 or 16 groups a
+    // step, eight steps an iteration, so the phase repeats).
     constexpr int kMem = NTW + 8;                         // memory ops per step
-    static_assert(kMem <= 4 * NTW, "two per group in the first half of the step");
-    auto step = [&](uint8_t *cur, uint8_t *ahead, int s, const QScales &sc, BFrag &bc,
-                    BFrag &bn, auto uconst, auto firstconst) {
+    constexpr int NG = 2 * NTW;                           // groups (kh, nt), kh major
+    // the group that issues memory op e: activations 0..7 in groups 0..7,
+    // the copies in the last NTW groups
+    auto op_group = [](int e) { return e < 8 ? e : e - 8 + (NG - NTW); };
+    static_assert(NG - NTW <= 8 && NTW >= 2, "schedule fits the step");
+    static_assert((8 * NG) % 4 == 0, "ring phase repeats every iteration");
+    v8i af[4];
+    auto issue = [&](const uint8_t *buf, int k, int slot) {   // group k's weight fragment
+        af[slot] = rd(buf + 2 * (k % NTW) * 2048, k / NTW);
+    };
+    auto step = [&](uint8_t *cur, uint8_t *next, uint8_t *ahead, int s, const QScales &sc,
+                    BFrag &bc, BFrag &bn, auto uconst, auto firstconst, auto phconst) {
         constexpr int U = decltype(uconst)::value;
         constexpr bool kFirst = decltype(firstconst)::value;
-        constexpr int NG = 2 * NTW;                       // groups (kh, nt), kh major
-        v8i af[3];
-        auto issue = [&](int k) {                         // group k's weight fragment
-            af[k % 3] = rd(cur + 2 * (k % NTW) * 2048, k / NTW);
-        };
-        issue(0);
-        issue(1);
-        __builtin_amdgcn_sched_barrier(0);               // the reads go out first
+        constexpr int PH = decltype(phconst)::value;
 #pragma unroll
         for (int k = 0; k < NG; ++k) {
 #pragma unroll
-            for (int e = 2 * k; e < 2 * k + 2; ++e) {
+            for (int e = 0; e < kMem; ++e) {
+                if (op_group(e) != k) continue;
                 if (e < 8) load_b_one(bn, s + 1, e);
-                else if (e < kMem) dma_one(ahead, s + 2, e - 8);
+                else dma_one(ahead, s + 2, e - 8);
             }
-            if (k + 2 < NG) issue(k + 2);
+            if (k == NG - 2) {
+                // this wavefront's copies of step s + 1 (issued during step
+                // s - 1, before all of this step's loads) have landed; of this
+                // step's loads, those of groups 0 .. NG - 2 are out: all but
+                // the last copy
+                static_assert(op_group(kMem - 2) <= NG - 2 && op_group(kMem - 1) == NG - 1,
+                              "kMem - 1 loads before the barrier");
+                __builtin_amdgcn_s_waitcnt(vmcnt_only(kMem - 1));
+                step_barrier();
+            }
+            if (k + 2 < NG) issue(cur, k + 2, (PH + k + 2) % 4);
+            else issue(next, k + 2 - NG, (PH + k + 2) % 4);
             __builtin_amdgcn_sched_barrier(0);
             const int kh = k / NTW, nt = k % NTW;
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt)
                 acc[nt][mt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    af[k % 3], bc[kh][mt], kFirst && kh == 0 ? v16f{} : acc[nt][mt], 0, 0, U,
-                    (int)sc.w[nt][kh], U, (int)sc.x[mt][kh]);
+                    af[(PH + k) % 4], bc[kh][mt], kFirst && kh == 0 ? v16f{} : acc[nt][mt], 0,
+                    0, U, (int)sc.w[nt][kh], U, (int)sc.x[mt][kh]);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // this wavefront's copies of step s + 1 (issued during step s - 1)
-        // have landed before any wavefront reads them; this step's kMem loads
-        // may still be in flight
-        static_assert(kMem < 64, "vmcnt holds 6 bits");
-        __builtin_amdgcn_s_waitcnt(vmcnt_only(kMem));
-        step_barrier();
     };
     using U0 = std::integral_constant<int, 0>;
     using U1 = std::integral_constant<int, 1>;
     using U2 = std::integral_constant<int, 2>;
     using U3 = std::integral_constant<int, 3>;
     using F0 = std::false_type;
+    using P0 = std::integral_constant<int, 0>;
+    using P2 = std::integral_constant<int, (NG % 4)>;    // the odd steps' phase
 
     // the workgroup's BN bias values, staged in LDS under the first barrier
     // (the bias needs only 2-byte alignment: one element per thread)
@@ -252,9 +268,11 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
 #pragma unroll
     for (int i = 0; i < NTW; ++i) dma_one(lds1, 1, i);
     // step 0's copies, activations and scales have landed; step 1's copies
-    // are checked at the end of step 0
+    // are checked at step 0's barrier
     __builtin_amdgcn_s_waitcnt(vmcnt_only(NTW));
     __syncthreads();
+    issue(lds0, 0, 0);
+    issue(lds0, 1, 1);
     // eight steps (two quads) per iteration: each LDS buffer and activation
     // register set is a fixed object and the two scale sets alternate without
     // copies; a step at or past S reads zeros and adds nothing
@@ -262,17 +280,17 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
         const int q = s / 4;
         load_qscales(q + 1, qb);
         if (s == 0)
-            step(lds0, lds2, s + 0, qa, ba, bb, U0{}, std::true_type{});
+            step(lds0, lds1, lds2, s + 0, qa, ba, bb, U0{}, std::true_type{}, P0{});
         else
-            step(lds0, lds2, s + 0, qa, ba, bb, U0{}, F0{});
-        step(lds1, lds3, s + 1, qa, bb, ba, U1{}, F0{});
-        step(lds2, lds0, s + 2, qa, ba, bb, U2{}, F0{});
-        step(lds3, lds1, s + 3, qa, bb, ba, U3{}, F0{});
+            step(lds0, lds1, lds2, s + 0, qa, ba, bb, U0{}, F0{}, P0{});
+        step(lds1, lds2, lds3, s + 1, qa, bb, ba, U1{}, F0{}, P2{});
+        step(lds2, lds3, lds0, s + 2, qa, ba, bb, U2{}, F0{}, P0{});
+        step(lds3, lds0, lds1, s + 3, qa, bb, ba, U3{}, F0{}, P2{});
         load_qscales(q + 2, qa);
-        step(lds0, lds2, s + 4, qb, ba, bb, U0{}, F0{});
-        step(lds1, lds3, s + 5, qb, bb, ba, U1{}, F0{});
-        step(lds2, lds0, s + 6, qb, ba, bb, U2{}, F0{});
-        step(lds3, lds1, s + 7, qb, bb, ba, U3{}, F0{});
+        step(lds0, lds1, lds2, s + 4, qb, ba, bb, U0{}, F0{}, P0{});
+        step(lds1, lds2, lds3, s + 5, qb, bb, ba, U1{}, F0{}, P2{});
+        step(lds2, lds3, lds0, s + 6, qb, ba, bb, U2{}, F0{}, P0{});
+        step(lds3, lds0, lds1, s + 7, qb, bb, ba, U3{}, F0{}, P2{});
     }
 
     // ---- epilogue, straight from registers: element i of lane (g, rr) in
