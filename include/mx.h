@@ -157,7 +157,14 @@ mx_status mx_quant_act_t16(int64_t M, int64_t K, const void *x, int64_t ldx, voi
  *     are restaged into it;
  *   otherwise 0 (MX_ACT_BF16, MX_ACT_MXFP8_T16, or pre-quantized M <= 64).
  * (K > 8192 with M <= 64 quantized inside the call is the exception: the
- * row-major staging round256(M * Kp) + round256(M * Kp / 32).) */
+ * row-major staging round256(M * Kp) + round256(M * Kp / 32).)
+ * E4M3 with M <= 64 quantized inside the call needs none when K % 128 == 0
+ * and the decode GEMV's launch plan divides the shape evenly (eight
+ * wavefronts of S / 8 steps each, S in {8, 16, 32, 56, 64}, whole tiles per
+ * workgroup): the quantization then runs inside the GEMV, with the same bytes
+ * and codes as mx_quant_act ([rocm_native] apply_weights fuses it at tiny
+ * M).  The environment variable MX_FUSED_QUANT=0, read once per process,
+ * turns that off; this function and mx_linear always agree. */
 mx_status mx_linear_workspace(int elem, int layout, int64_t N, int64_t K,
                               int64_t M, int act, int prequantized,
                               size_t *bytes);

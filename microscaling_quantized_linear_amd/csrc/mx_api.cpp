@@ -43,6 +43,19 @@ mx::GemvW8Plan gemv_w8_plan(int64_t N, int64_t K, int64_t M) {
 }
 int64_t padded_k(int64_t K) { return (K + 127) / 128 * 128; }
 
+// In-call quantization inside the decode GEMV (one launch, no workspace):
+// W8A8 with M <= 64 whose shape the GEMV plan divides evenly and K % 128 == 0.
+// MX_FUSED_QUANT=0 switches it off (then a quantization launch into the
+// workspace precedes the GEMV); read once.
+bool fused_quant_ok(int elem, int64_t N, int64_t K, int64_t M) {
+    static const bool enabled = [] {
+        const char *s = std::getenv("MX_FUSED_QUANT");
+        return !(s && s[0] == '0');
+    }();
+    return enabled && elem == E4M3 && M <= kGemvMaxM && K % 128 == 0 &&
+           mx::gemv_w8_even(N, K, gemv_w8_plan(N, K, M));
+}
+
 mx_status shape_ok(int elem, int layout, int64_t E, int64_t N, int64_t K) {
     if (elem != E4M3 && elem != E2M1) return MX_ERR_UNSUPPORTED;
     if (layout != ROW32 && layout != BLK32) return MX_ERR_UNSUPPORTED;
@@ -205,6 +218,8 @@ mx_status mx_linear_workspace(int elem, int layout, int64_t N, int64_t K, int64_
     if (act != ACT_BF16 && act != ACT_MXFP8 && act != ACT_MXFP8_T16) return MX_ERR_UNSUPPORTED;
     *bytes = 0;
     const bool long_k = M <= kGemvMaxM && !gemv_w8_plan(N, K, M).ok;
+    if (act == ACT_MXFP8 && !prequantized && fused_quant_ok(elem, N, K, M))
+        return MX_OK;                                   // quantized inside the GEMV
     if (act == ACT_MXFP8 && !prequantized && !long_k)   // in-call quantization into T16
         *bytes = (size_t)(round256(mx::act_t16_data_bytes(M, K)) + mx::act_codes_t16_bytes(M, K));
     else if (act == ACT_MXFP8 && !prequantized)         // row-major, chunked GEMV for long K
@@ -265,6 +280,20 @@ mx_status mx_linear(int elem, int layout, int64_t N, int64_t K, const void *w_pa
     int64_t lq = ldq, lc = ldc;
     bool a16 = t16;
     const mx::GemvW8Plan w8 = gemv_w8_plan(N, K, M);
+    if (incall && !gemm && fused_quant_ok(elem, N, K, M)) {
+        mx::GemvW8Args g{};
+        g.w = static_cast<const uint8_t *>(w_packed);
+        g.codes = static_cast<const uint8_t *>(codes_packed);
+        g.N = N;
+        g.K = K;
+        g.M = M;
+        g.xb = static_cast<const uint16_t *>(x);
+        g.ldx = ldx;
+        g.bias = static_cast<const uint16_t *>(bias);
+        g.y = static_cast<uint16_t *>(y);
+        g.ldy = ldy;
+        return launched(mx::launch_gemv_w8_fused(layout, rule, g, w8, s));
+    }
     if (incall && !gemm && !w8.ok) {
         // K beyond the T16 GEMV's registers: row-major quantization into ws
         // for the chunked GEMV

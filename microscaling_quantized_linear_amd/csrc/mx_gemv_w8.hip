@@ -213,6 +213,369 @@ __global__ void __launch_bounds__(512) gemv_w8_kernel(GemvW8Args p) {
     }
 }
 
+// The same product when the shape divides evenly and the activations come
+// in the T16 layout: every wavefront owns exactly SPW steps and every
+// workgroup G whole tiles, so no load needs a guard (T16 pads tokens past M
+// and K past its end with zero bytes and code 127).  What differs is the
+// front of the kernel: offsets are 32-bit with their uniform parts in scalar
+// registers, and the first step's weight chunks are requested before
+// anything else, so the weight stream starts at the top of the kernel; the
+// activation copies and both codes follow, then the remaining weight chunks.
+// Measured on MI355X, every cycle between the start of a wavefront and its
+// weight requests adds to the time of this HBM-bound kernel.
+template <int LAYOUT, int G, int SPW, int NW>
+__global__ void __launch_bounds__(NW * 64) gemv_w8_even_kernel(GemvW8Args p) {
+    constexpr int NQ = (SPW + 6) / 4;                   // quads SPW steps can span
+    static_assert(2 * G * (SPW - 1) < 64, "vmcnt holds 6 bits");
+    __shared__ __attribute__((aligned(1024))) uint8_t xs[NW][SPW * 2048];
+    __shared__ v4f red[NW][G][64];
+
+    const int lane = threadIdx.x % 64;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int r = lane % 16, j = lane / 16;
+    const uint32_t S = (uint32_t)((p.K + 127) / 128), Q = (S + 3) / 4;
+    const uint32_t MB = gridDim.y, mb = blockIdx.y;
+    const uint32_t t0 = blockIdx.x * G;
+    const uint32_t s0 = wave * SPW, qa = s0 / 4;
+    const uint32_t lo = 16 * lane;
+
+    // ---- 1. the first step's weight chunks ----
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w + (size_t)t0 * S * 2048, G * S * 2048);
+    v4u wv[SPW][G][2];
+    auto wload = [&](int i) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                wv[i][g][h] = __builtin_amdgcn_raw_buffer_load_b128(
+                    wr, lo, (int)((g * S + s0 + i) * 2048 + h * 1024), kNT);
+    };
+    wload(0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 2. activation fragments of the wavefront's steps -> its LDS ----
+    uint8_t *myx = xs[wave];
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.xf, MB * S * 2048);
+#pragma unroll
+    for (int i = 0; i < SPW; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xr, (lds_void_w8 *)(myx + (2 * i + h) * 1024), 16, (int)lo,
+                (int)(((mb * S + s0 + i) * 2 + h) * 1024), 0, 0);
+
+    // ---- 3. codes: one dword per quad of steps (byte u = step 4 q + u) ----
+    // A quad past the last one reads zero through the resource bounds and is
+    // never used.
+    const __amdgpu_buffer_rsrc_t xcr = make_rsrc(p.xct, MB * Q * 256);
+    uint32_t cxq[NQ];
+#pragma unroll
+    for (int c = 0; c < NQ; ++c)
+        cxq[c] = __builtin_amdgcn_raw_buffer_load_b32(xcr, 4 * lane, (int)((mb * Q + qa + c) * 256), 0);
+    uint32_t cwq[G][NQ];
+    if constexpr (LAYOUT == BLK32) {
+        // tiles 2 R and 2 R + 1 share the codes of row group R
+        const __amdgpu_buffer_rsrc_t cr = make_rsrc(p.codes, (uint32_t)(p.N / 32) * Q * 16);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int c = 0; c < NQ; ++c) {
+                if (G % 2 == 0 && g % 2 == 1) {
+                    cwq[g][c] = cwq[g - 1][c];
+                    continue;
+                }
+                cwq[g][c] = __builtin_amdgcn_raw_buffer_load_b32(
+                    cr, 4 * j, (int)((((t0 + g) / 2) * Q + qa + c) * 16), 0);
+            }
+    } else {
+        const __amdgpu_buffer_rsrc_t cr = make_rsrc(p.codes, (uint32_t)(p.N / 16) * Q * 256);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int c = 0; c < NQ; ++c)
+                cwq[g][c] = __builtin_amdgcn_raw_buffer_load_b32(
+                    cr, 4 * lane, (int)(((t0 + g) * Q + qa + c) * 256), 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 4. the remaining weight chunks ----
+#pragma unroll
+    for (int i = 1; i < SPW; ++i) wload(i);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Everything before the remaining weight chunks has landed once at most
+    // that many loads are outstanding (in-order completion); the compiler
+    // does not count the copies into LDS, hence the explicit wait.
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * G * (SPW - 1)));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 5. one scaled MFMA per tile and step ----
+    v4f acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
+    auto run = [&](auto aconst) {
+        constexpr int A = decltype(aconst)::value;
+        static_for<0, SPW>([&](auto iconst) {
+            constexpr int i = decltype(iconst)::value;
+            constexpr int c = (A + i) / 4, u = (A + i) % 4;
+            const v4u b0 = *reinterpret_cast<const v4u *>(myx + (2 * i) * 1024 + 16 * lane);
+            const v4u b1 = *reinterpret_cast<const v4u *>(myx + (2 * i + 1) * 1024 + 16 * lane);
+            const v8i bf = cat8(b0, b1);
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+                acc[g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    cat8(wv[i][g][0], wv[i][g][1]), bf, acc[g], 0, 0, u, (int)cwq[g][c], u,
+                    (int)cxq[c]);
+        });
+    };
+    switch (s0 % 4) {
+    case 0: run(std::integral_constant<int, 0>{}); break;
+    case 1: run(std::integral_constant<int, 1>{}); break;
+    case 2: run(std::integral_constant<int, 2>{}); break;
+    default: run(std::integral_constant<int, 3>{}); break;
+    }
+
+    // ---- 6. wavefront-order reduction; wavefront g finishes tile g ----
+#pragma unroll
+    for (int g = 0; g < G; ++g) red[wave][g][lane] = acc[g];
+    __syncthreads();
+    if (wave >= G) return;
+    const int g = wave;
+    v4f a = red[0][g][lane];
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) a += red[w2][g][lane];
+    const int64_t row = 16 * (int64_t)mb + r;
+    if (row >= p.M) return;
+    // lane (r, j) holds rows 4 j .. 4 j + 3 of the tile for token r
+    const int64_t n0 = 16 * (int64_t)(t0 + g) + 4 * j;
+    float v[4] = {a[0], a[1], a[2], a[3]};
+    if (p.bias)
+        for (int e = 0; e < 4; ++e) v[e] += bf16_to_f32(p.bias[n0 + e]);
+    v2u o = {bf16_bits(v[0]) | (bf16_bits(v[1]) << 16), bf16_bits(v[2]) | (bf16_bits(v[3]) << 16)};
+    *reinterpret_cast<v2u *>(p.y + row * p.ldy + n0) = o;
+}
+
+// The even-shape GEMV with the per-token MXFP8 quantization of the bf16
+// activations done inside it ([rocm_native] apply_weights: at tiny M the
+// quantization is fused into the product).  Each wavefront quantizes exactly
+// the activation fragment it multiplies.  Lane (r, j) must end with token
+// 16 mb + r, K 128 s + 16 j + [0, 16) and 128 s + 64 + 16 j + [0, 16): two
+// halves of two 32-value blocks, whose other halves sit in the lane 16 apart.
+//
+// Loads: per step, four 1 KB loads of 4 tokens x 256 contiguous bytes (lane
+// l reads token 4 u + l / 16, bytes 16 (l % 16) of the step).  Reading 16
+// tokens x 64 bytes per load instead, with the caller's row stride, measured
+// about 4 us slower per launch on MI355X.  A padded 16 x 272-byte LDS tile per
+// wavefront turns the loads into the fragment order (rows 272 bytes apart
+// keep both the writes and the 16-byte reads free of bank conflicts).
+//
+// Quantization: quant_half_block_cvt, the scaled hardware convert, which
+// gives the bytes of mx_quant_act.  The MFMA's activation scale for lane
+// (r, j) is the code of block j of the step, which a lane pair computes; one
+// lane permute brings it to the lane that needs it.
+//
+// Order: the raw activations of all the wavefront's steps first (L2 hits,
+// they arrive long before the weights), then the weight chunks of the first
+// step and the weight codes; each step is quantized just before its MFMAs,
+// after which the next step's weight chunks are requested.  One step of
+// weight chunks in flight per wavefront (1,792 wavefronts, 7 MB in flight)
+// measured fastest on MI355X: deeper windows, and activations requested with
+// the weights of their step instead of all first, were slower.  Results are
+// identical to mx_quant_act_t16 followed by the even-shape kernel: the same
+// bytes, codes and MFMA order.
+template <int LAYOUT, int RULE, int G, int SPW, int NW>
+__global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
+    constexpr int WIN = 1;                             // steps of weight chunks in flight
+    constexpr int XROW = 272;                          // padded LDS row of one token
+    __shared__ v4f red[NW][G][64];
+    __shared__ __attribute__((aligned(16))) uint8_t xt[NW][16 * XROW];
+
+    const int lane = threadIdx.x % 64;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int r = lane % 16, j = lane / 16;
+    const uint32_t S = (uint32_t)(p.K / 128), Q = (S + 3) / 4;
+    const uint32_t mb = blockIdx.y;
+    const uint32_t t0 = blockIdx.x * G;
+    const uint32_t s0 = wave * SPW;
+    const uint32_t lo = 16 * lane;
+
+    // ---- 1. raw bf16 activations of the wavefront's steps ----
+    // load u of a step: token 16 mb + 4 u + j, bytes 16 r of the step's 256;
+    // tokens past M read zeros through the resource bounds
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.xb, (uint32_t)(p.M * p.ldx * 2));
+    uint32_t xo[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t tok = 16 * (int64_t)mb + 4 * u + j;
+        xo[u] = tok < p.M ? (uint32_t)(tok * p.ldx * 2) + 16 * r : kOOB;
+    }
+    v4u xv[SPW][4];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            xv[i][u] = __builtin_amdgcn_raw_buffer_load_b128(xr, xo[u], (int)(256 * (s0 + i)), 0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 2. the first WIN steps of weight chunks ----
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w + (size_t)t0 * S * 2048, G * S * 2048);
+    v4u wv[SPW][G][2];
+    auto wload = [&](int i) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                wv[i][g][h] = __builtin_amdgcn_raw_buffer_load_b128(
+                    wr, lo, (int)((g * S + s0 + i) * 2048 + h * 1024), kNT);
+    };
+#pragma unroll
+    for (int i = 0; i < WIN; ++i) wload(i);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 3. weight codes: the byte of each step (byte u of a code dword is
+    // step 4 q + u), loaded as a byte so no register array is indexed by the
+    // wavefront's runtime quad offset ----
+    uint32_t cws[SPW][G];
+    if constexpr (LAYOUT == BLK32) {
+        // tiles 2 R and 2 R + 1 share the codes of row group R
+        const __amdgpu_buffer_rsrc_t cr = make_rsrc(p.codes, (uint32_t)(p.N / 32) * Q * 16);
+#pragma unroll
+        for (int i = 0; i < SPW; ++i)
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (G % 2 == 0 && g % 2 == 1) {
+                    cws[i][g] = cws[i][g - 1];
+                    continue;
+                }
+                const uint32_t s = s0 + i;
+                cws[i][g] = __builtin_amdgcn_raw_buffer_load_b8(
+                    cr, 4 * j, (int)((((t0 + g) / 2) * Q + s / 4) * 16 + s % 4), 0);
+            }
+    } else {
+        const __amdgpu_buffer_rsrc_t cr = make_rsrc(p.codes, (uint32_t)(p.N / 16) * Q * 256);
+#pragma unroll
+        for (int i = 0; i < SPW; ++i)
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const uint32_t s = s0 + i;
+                cws[i][g] = __builtin_amdgcn_raw_buffer_load_b8(
+                    cr, 4 * lane, (int)(((t0 + g) * Q + s / 4) * 256 + s % 4), 0);
+            }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 4. per step: transpose, quantize, one scaled MFMA per tile, refill ----
+    // Lane j computes the codes of blocks j/2 (first half) and 2 + j/2
+    // (second half); the MFMA wants block j: lanes j = 0 and 3 hold it, lane
+    // j = 1 takes the first-half code of lane j = 2, lane j = 2 the
+    // second-half code of lane j = 1.
+    uint8_t *tile = xt[wave];
+    const int src = j == 1 ? lane + 16 : (j == 2 ? lane - 16 : lane);
+    v4f acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
+    static_for<0, SPW>([&](auto iconst) {
+        constexpr int i = decltype(iconst)::value;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            *reinterpret_cast<v4u *>(tile + (4 * u + j) * XROW + 16 * r) = xv[i][u];
+        const uint8_t *mine = tile + r * XROW + 32 * j;
+        const v4u f0 = *reinterpret_cast<const v4u *>(mine);
+        const v4u f1 = *reinterpret_cast<const v4u *>(mine + 16);
+        const v4u f2 = *reinterpret_cast<const v4u *>(mine + 128);
+        const v4u f3 = *reinterpret_cast<const v4u *>(mine + 144);
+        uint32_t c0, c1;
+        const v4u q0 = quant_half_block_cvt<RULE>(f0, f1, c0);
+        const v4u q1 = quant_half_block_cvt<RULE>(f2, f3, c1);
+        const v8i bq = cat8(q0, q1);
+        const uint32_t got = (uint32_t)__shfl((int)(j == 2 ? c0 : c1), src);
+        const uint32_t cx = j == 0 ? c0 : (j == 3 ? c1 : got);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            acc[g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                cat8(wv[i][g][0], wv[i][g][1]), bq, acc[g], 0, 0, 0, (int)cws[i][g], 0,
+                (int)cx);
+        // the refill goes out right behind this step's MFMAs (left alone,
+        // the scheduler sinks it next to its use and exposes its latency)
+        if constexpr (i + WIN < SPW) wload(i + WIN);
+        __builtin_amdgcn_sched_barrier(0);
+    });
+
+    // ---- 5. wavefront-order reduction; wavefront g finishes tile g ----
+#pragma unroll
+    for (int g = 0; g < G; ++g) red[wave][g][lane] = acc[g];
+    __syncthreads();
+    const int64_t row = 16 * (int64_t)mb + r;
+    if (wave >= G || row >= p.M) return;
+    const int g = wave;
+    v4f a = red[0][g][lane];
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) a += red[w2][g][lane];
+    const int64_t n0 = 16 * (int64_t)(t0 + g) + 4 * j;
+    float v[4] = {a[0], a[1], a[2], a[3]};
+    if (p.bias)
+        for (int e = 0; e < 4; ++e) v[e] += bf16_to_f32(p.bias[n0 + e]);
+    v2u o = {bf16_bits(v[0]) | (bf16_bits(v[1]) << 16), bf16_bits(v[2]) | (bf16_bits(v[3]) << 16)};
+    *reinterpret_cast<v2u *>(p.y + row * p.ldy + n0) = o;
+}
+
+// launch helpers of the even-shape kernels: SPW in {1, 2, 4, 7, 8}, G in
+// {1, 2, 4} with G * SPW <= 16, eight wavefronts
+template <int G, class F>
+static hipError_t even_spw(int spw, F &&f) {
+    switch (spw) {
+    case 1: return f(std::integral_constant<int, G>{}, std::integral_constant<int, 1>{});
+    case 2: return f(std::integral_constant<int, G>{}, std::integral_constant<int, 2>{});
+    case 4: return f(std::integral_constant<int, G>{}, std::integral_constant<int, 4>{});
+    case 7:
+        if constexpr (G * 7 <= 16) return f(std::integral_constant<int, G>{}, std::integral_constant<int, 7>{});
+        break;
+    case 8:
+        if constexpr (G * 8 <= 16) return f(std::integral_constant<int, G>{}, std::integral_constant<int, 8>{});
+        break;
+    default: break;
+    }
+    return hipErrorInvalidValue;
+}
+template <class F>
+static hipError_t even_dispatch(const GemvW8Plan &pl, F &&f) {
+    switch (pl.g) {
+    case 1: return even_spw<1>(pl.spw, f);
+    case 2: return even_spw<2>(pl.spw, f);
+    case 4: return even_spw<4>(pl.spw, f);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+bool gemv_w8_even(int64_t N, int64_t K, const GemvW8Plan &pl) {
+    const int64_t S = (K + 127) / 128, T = N / 16;
+    return pl.ok && pl.nw == 8 && S == 8 * (int64_t)pl.spw && T % pl.g == 0 &&
+           pl.g * pl.spw <= 16;
+}
+
+hipError_t launch_gemv_w8_fused(int layout, int rule, const GemvW8Args &a, const GemvW8Plan &pl,
+                                hipStream_t st) {
+    if (!gemv_w8_even(a.N, a.K, pl) || a.K % 128 != 0) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(a.N / 16 / pl.g), (unsigned)((a.M + 15) / 16)), block(512);
+    const hipError_t e = even_dispatch(pl, [&](auto gc, auto sc) -> hipError_t {
+        constexpr int G = decltype(gc)::value, SPW = decltype(sc)::value;
+        if (layout == ROW32) {
+            if (rule == RULE_OCP)
+                hipLaunchKernelGGL((gemv_w8_fused_kernel<ROW32, RULE_OCP, G, SPW, 8>), grid, block, 0, st, a);
+            else
+                hipLaunchKernelGGL((gemv_w8_fused_kernel<ROW32, RULE_CEIL448, G, SPW, 8>), grid, block, 0, st, a);
+        } else {
+            if (rule == RULE_OCP)
+                hipLaunchKernelGGL((gemv_w8_fused_kernel<BLK32, RULE_OCP, G, SPW, 8>), grid, block, 0, st, a);
+            else
+                hipLaunchKernelGGL((gemv_w8_fused_kernel<BLK32, RULE_CEIL448, G, SPW, 8>), grid, block, 0, st, a);
+        }
+        return hipSuccess;
+    });
+    if (e != hipSuccess) return e;
+    return hipGetLastError();
+}
+
 template <int LAYOUT, bool XFRAG, int G>
 static hipError_t launch_w8_spw(const GemvW8Args &a, const GemvW8Plan &pl, hipStream_t st) {
     const dim3 grid((unsigned)((a.N / 16 + G - 1) / G), (unsigned)((a.M + 15) / 16));
@@ -249,6 +612,19 @@ static hipError_t launch_w8_g(const GemvW8Args &a, const GemvW8Plan &pl, hipStre
 
 hipError_t launch_gemv_w8(int layout, bool xfrag, const GemvW8Args &a, const GemvW8Plan &pl,
                           hipStream_t st) {
+    if (xfrag && gemv_w8_even(a.N, a.K, pl)) {
+        const dim3 grid((unsigned)(a.N / 16 / pl.g), (unsigned)((a.M + 15) / 16)), block(512);
+        const hipError_t e = even_dispatch(pl, [&](auto gc, auto sc) -> hipError_t {
+            constexpr int G = decltype(gc)::value, SPW = decltype(sc)::value;
+            if (layout == ROW32)
+                hipLaunchKernelGGL((gemv_w8_even_kernel<ROW32, G, SPW, 8>), grid, block, 0, st, a);
+            else
+                hipLaunchKernelGGL((gemv_w8_even_kernel<BLK32, G, SPW, 8>), grid, block, 0, st, a);
+            return hipSuccess;
+        });
+        if (e != hipSuccess) return e;
+        return hipGetLastError();
+    }
     if (layout == ROW32)
         return xfrag ? launch_w8_g<ROW32, true>(a, pl, st) : launch_w8_g<ROW32, false>(a, pl, st);
     return xfrag ? launch_w8_g<BLK32, true>(a, pl, st) : launch_w8_g<BLK32, false>(a, pl, st);

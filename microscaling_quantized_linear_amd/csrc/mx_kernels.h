@@ -82,6 +82,8 @@ struct GemvW8Args {
     const uint8_t *xc;
     int64_t ldc;
     const uint8_t *xf, *xct;
+    const uint16_t *xb;            // bf16 activations [M, ldx] (fused quantization)
+    int64_t ldx;
     const uint16_t *bias;
     uint16_t *y;
     int64_t ldy;
@@ -95,6 +97,14 @@ struct GemvW8Plan {
 GemvW8Plan plan_gemv_w8(int64_t T, int64_t S, int64_t MB, int nw_force, int g_force);
 hipError_t launch_gemv_w8(int layout, bool xt16, const GemvW8Args &a, const GemvW8Plan &plan,
                           hipStream_t stream);
+// True when the plan divides the shape evenly: eight wavefronts of exactly
+// `spw` steps, whole tiles per workgroup.  Then T16 input runs the even-shape
+// kernel, and bf16 input with K % 128 == 0 can be quantized inside the GEMV.
+bool gemv_w8_even(int64_t N, int64_t K, const GemvW8Plan &plan);
+// Per-token quantization fused into the GEMV (a.xb, a.ldx bf16 input; rule as
+// in mx_quant_act); requires gemv_w8_even and K % 128 == 0.
+hipError_t launch_gemv_w8_fused(int layout, int rule, const GemvW8Args &a,
+                                const GemvW8Plan &plan, hipStream_t stream);
 
 // per-token quantization into the T16 layout (mx_quant.hip)
 hipError_t launch_quant_t16(int64_t M, int64_t K, const void *x, int64_t ldx, void *xq,

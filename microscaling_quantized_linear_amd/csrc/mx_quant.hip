@@ -29,20 +29,6 @@ __device__ inline uint32_t quad_max(uint32_t v) {
 }
 
 template <int RULE>
-__device__ inline uint32_t act_code(uint32_t amax_bits /* fp32 bits, sign 0 */) {
-    const int e = (int)(amax_bits >> 23);          // exponent field; 0 for 0 and subnormals
-    int c;
-    if (RULE == RULE_OCP) {
-        c = e - 8;                                 // floor(log2 amax) - 8 + 127
-    } else {
-        c = e - 8 + ((amax_bits & 0x7FFFFFu) > 0x600000u ? 1 : 0);   // mantissa > 1.75
-    }
-    if (e == 0) c = 0;                             // amax < 2^-126 -> code 0 (both rules)
-    c = c < 0 ? 0 : c;
-    return (uint32_t)(c > 254 ? 254 : c);
-}
-
-template <int RULE>
 __global__ void __launch_bounds__(256) quant_act_kernel(
     int64_t M, int64_t K, const uint16_t *__restrict__ x, int64_t ldx,
     uint8_t *__restrict__ xq, int64_t ldq, uint8_t *__restrict__ xcodes, int64_t ldc) {
@@ -118,32 +104,8 @@ __global__ void __launch_bounds__(256) quant_act_t16_kernel(
         v[0] = *reinterpret_cast<const v4u *>(x + m * ldx + k0);
         v[1] = *reinterpret_cast<const v4u *>(x + m * ldx + k0 + 8);
     }
-    uint32_t amax = 0;
-    for (int a = 0; a < 2; ++a)
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = (v[a][i] & 0x7FFFu) << 16, hi = (v[a][i] >> 16 & 0x7FFFu) << 16;
-            amax = amax > lo ? amax : lo;
-            amax = amax > hi ? amax : hi;
-        }
-    const uint32_t other = (uint32_t)__shfl_xor((int)amax, 16);
-    amax = amax > other ? amax : other;
-    const uint32_t code = act_code<RULE>(amax);
-    const float mul = __uint_as_float((254u - code) << 23);
-    uint32_t out[4];
-    for (int a = 0; a < 2; ++a)
-        for (int d = 0; d < 2; ++d) {
-            float f[4];
-            for (int i = 0; i < 2; ++i) {
-                const uint32_t w = v[a][2 * d + i];
-                f[2 * i] = __uint_as_float(w << 16) * mul;
-                f[2 * i + 1] = __uint_as_float(w & 0xFFFF0000u) * mul;
-            }
-            for (int i = 0; i < 4; ++i) f[i] = __builtin_fminf(__builtin_fmaxf(f[i], -448.0f), 448.0f);
-            int packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-            packed = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], packed, true);
-            out[2 * a + d] = (uint32_t)packed;
-        }
-    v4u o = {out[0], out[1], out[2], out[3]};
+    uint32_t code;
+    const v4u o = quant_half_block<RULE>(v[0], v[1], code);
     *reinterpret_cast<v4u *>(xq + ((mb * S + s) * 2 + h) * 1024 + 16 * lane) = o;
     // the even lane of each pair writes the block's code
     if (j % 2 == 0) {

@@ -110,6 +110,14 @@ def test_linear_validation_paths():
     assert mx.mx_linear_workspace(0, 0, 64, 256, 4, 0, 0) == 0
     # the prefill GEMM restages the activation codes even when pre-quantized
     assert mx.mx_linear_workspace(0, 0, 64, 256, 65, 1, 1) > 0
+    # quantization inside the decode GEMV (K % 128 == 0, S = K / 128 in
+    # {8, 16, 32, 56, 64}, even tiles): no workspace
+    for layout, N, K, M in [(1, 7168, 7168, 16), (0, 256, 1024, 4), (1, 64, 8192, 64),
+                            (0, 96, 2048, 1)]:
+        assert mx.mx_linear_workspace(0, layout, N, K, M, 1, 0) == 0, (layout, N, K, M)
+    # K = 1536 (S = 12) and K = 1568 (ragged) stay with a quantization launch
+    assert mx.mx_linear_workspace(0, 1, 256, 1536, 4, 1, 0) > 0
+    assert mx.mx_linear_workspace(0, 0, 256, 1568, 4, 1, 0) > 0
     # a valid call on a machine without a gfx950 device stops at the gate
     import torch
     if not torch.cuda.is_available():

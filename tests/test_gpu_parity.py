@@ -348,3 +348,35 @@ def test_linear_t16_equals_in_call(g, layout, M, N, K):
     oq, oc = oracle.quant_act(x, OCP)
     ref = oracle.linear(E4M3, layout, N, K, w, codes, M, MXFP8, xq=oq, xcodes=oc, bias=b)
     g.assert_close(y, ref, "T16 activation")
+
+
+# ------------------------------------------------------------------ fused quantization
+
+FUSED_SHAPES = [(1, 64, 1024), (2, 96, 2048), (15, 256, 4096), (16, 1792, 7168), (17, 64, 8192),
+                (33, 32, 1024), (64, 128, 2048), (4, 7168, 7168)]
+
+
+@pytest.mark.parametrize("layout", [ROW32, BLK32])
+@pytest.mark.parametrize("M,N,K", FUSED_SHAPES)
+def test_fused_quant_gemv(g, layout, M, N, K):
+    """Quantization inside the decode GEMV (no workspace) gives the result of
+    mx_quant_act_t16 followed by the GEMV on it, and of the row-major
+    pre-quantized path, bit for bit, under both rules; within the bar of the
+    oracle."""
+    import microscaling_quantized_linear_amd as mx
+    if layout == BLK32 and N % 32:
+        pytest.skip("BLK32 needs N % 32 == 0")
+    assert mx.mx_linear_workspace(E4M3, layout, N, K, M, MXFP8, 0) == 0
+    w, codes, x, bias = _dense_inputs([45, M, N, K, layout], E4M3, layout, M, N, K)
+    wp, cp = g.pack(E4M3, layout, 1, N, K, w, codes)
+    for rule in (OCP, CEIL):
+        b = bias if (M + rule) % 2 else None
+        y = g.linear(E4M3, layout, N, K, wp, cp, MXFP8, x=x, rule=rule, bias=b)
+        xq, xc = g.quant_t16(x, rule)
+        y16 = g.linear(E4M3, layout, N, K, wp, cp, MXFP8_T16, xq=xq, xcodes=xc, bias=b, M=M)
+        assert np.array_equal(y, y16), "fused != T16 path"
+        oq, oc = oracle.quant_act(x, rule)
+        yr = g.linear(E4M3, layout, N, K, wp, cp, MXFP8, xq=oq, xcodes=oc, bias=b)
+        assert np.array_equal(y, yr), "fused != row-major pre-quantized path"
+        ref = oracle.linear(E4M3, layout, N, K, w, codes, M, MXFP8, xq=oq, xcodes=oc, bias=b)
+        g.assert_close(y, ref, f"fused quant rule {rule}")
