@@ -380,3 +380,67 @@ def test_fused_quant_gemv(g, layout, M, N, K):
         assert np.array_equal(y, yr), "fused != row-major pre-quantized path"
         ref = oracle.linear(E4M3, layout, N, K, w, codes, M, MXFP8, xq=oq, xcodes=oc, bias=b)
         g.assert_close(y, ref, f"fused quant rule {rule}")
+
+
+# ------------------------------------------------------------------ more MoE shapes
+
+MOE_SHAPES = [
+    # elem, E, N, K, T, topk
+    (E2M1, 8, 64, 1024, 5, 2),
+    (E2M1, 16, 128, 3072, 16, 8),
+    (E2M1, 12, 96, 992, 7, 3),        # K % 128 != 0: padded tail
+    (E4M3, 4, 48, 2048, 6, 2),
+    (E4M3, 5, 32, 3072, 16, 4),
+    (E2M1, 64, 16, 1024, 16, 8),      # one tile per expert, many experts per workgroup
+    (E2M1, 300, 16, 1024, 4, 4),
+]
+
+
+@pytest.mark.parametrize("elem,E,N,K,T,topk", MOE_SHAPES)
+def test_moe_shapes(g, elem, E, N, K, T, topk):
+    """The grouped GEMV at further shapes: long K, a ragged K tail, e4m3
+    weights, one tile per expert with many experts; per-slot and combined,
+    deterministic, against the oracle."""
+    rng = np.random.default_rng([62, elem, E, N, K, T, topk])
+    if elem == E2M1:
+        w = wl.fp4_bytes(rng, (E, N, K // 2))
+    else:
+        w = wl.e4m3_bytes(rng, (E, N, K))
+    codes = wl.codes(rng, (E * N, K // 32), 120, 132)
+    x = wl.activations(rng, (T, K))
+    ids, wts = wl.routing(rng, T, E, topk)
+    wp, cp = g.pack(elem, ROW32, E, N, K, w, codes)
+    ref = oracle.moe_linear(elem, E, N, K, w, codes, x, ids)
+    y = g.moe(elem, E, N, K, wp, cp, x, ids)
+    g.assert_close(y, ref, "moe")
+    assert np.array_equal(y, g.moe(elem, E, N, K, wp, cp, x, ids)), "not deterministic"
+    refc = oracle.moe_linear(elem, E, N, K, w, codes, x, ids, wts)
+    yc = g.moe(elem, E, N, K, wp, cp, x, ids, wts)
+    g.assert_close(yc, refc, "moe combined")
+
+
+def test_moe_edges_long_k(g):
+    """Routing edges at K = 1024: an expert with 40 slots (three batches of
+    16), ids out of range (zero rows), a duplicate id, an expert nobody routes
+    to, and no valid id at all."""
+    E, N, K, T, topk = 6, 32, 1024, 40, 2
+    d = wl.moe_inputs(4, E=E, N=N, K=K, T=T, topk=topk, seed=3)
+    ids = d["ids"].copy()
+    ids[:, 0] = 0
+    ids[1, 1] = -3
+    ids[2, 1] = E
+    ids[3, 1] = 0
+    ids[ids == 5] = 4
+    wp, cp = g.pack(E2M1, ROW32, E, N, K, d["w"], d["codes"])
+    ref = oracle.moe_linear(E2M1, E, N, K, d["w"], d["codes"], d["x"], ids)
+    y = g.moe(E2M1, E, N, K, wp, cp, d["x"], ids)
+    g.assert_close(y, ref, "moe edges")
+    yv = y.reshape(T, topk, N)
+    assert np.all(yv[1, 1] == 0) and np.all(yv[2, 1] == 0)
+    assert np.array_equal(yv[3, 0], yv[3, 1])
+    refc = oracle.moe_linear(E2M1, E, N, K, d["w"], d["codes"], d["x"], ids, d["weights"])
+    yc = g.moe(E2M1, E, N, K, wp, cp, d["x"], ids, d["weights"])
+    g.assert_close(yc, refc, "moe edges combined")
+    # no valid id at all: every row zero
+    bad = np.full_like(ids, -1)
+    assert not g.moe(E2M1, E, N, K, wp, cp, d["x"], bad).any()
