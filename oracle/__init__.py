@@ -74,6 +74,14 @@ def _declare(L):
     L.orc_moe_linear.argtypes = [i32, i64, i64, i64, p, p, i64, i64, p, i64, p,
                                  p, p]
     L.orc_moe_linear.restype = None
+    L.orc_moe_copies.argtypes = [i32, i64, i64, i64, i64, i64, p, p, p, p, p, p, p, p]
+    L.orc_moe_copies.restype = i32
+    L.orc_silu.argtypes = [dbl]; L.orc_silu.restype = dbl
+    L.orc_bf16_round.argtypes = [dbl]; L.orc_bf16_round.restype = C.c_uint16
+    L.orc_moe_gate_up.argtypes = [i32, i64, i64, i64, p, p, i64, i64, p, i64, p, p]
+    L.orc_moe_gate_up.restype = None
+    L.orc_moe_linear_rows.argtypes = [i32, i64, i64, i64, p, p, i64, i64, p, i64, p, p, p]
+    L.orc_moe_linear_rows.restype = None
     L.orc_threads.argtypes = []
     L.orc_threads.restype = i32
 
@@ -201,6 +209,70 @@ def moe_linear(elem, E, N, K, w, codes, x, ids, weights=None):
     y = np.empty(shape, np.float64)
     lib().orc_moe_linear(elem, E, N, K, _ptr(w), _ptr(codes), T, topk, _ptr(x),
                          x.shape[1], _ptr(ids), _ptr(weights), _ptr(y))
+    return y
+
+
+def moe_copies(elem, E, Np, inter, K, H, w13, s13, w2, s2):
+    """The load-time expert copies: interleaved w13 [E, 2 inter, rowb] with
+    codes [E, 2 inter, K/32], and w2 cut to [E, H, inter values] with codes
+    [E, H, inter/32].  Raises ValueError when the weights' padding is not zero."""
+    w13, s13, w2, s2 = (_c(a, np.uint8) for a in (w13, s13, w2, s2))
+    rowb = K // 2 if elem == E2M1 else K
+    r2 = inter // 2 if elem == E2M1 else inter
+    ow13 = np.empty((E, 2 * inter, rowb), np.uint8)
+    os13 = np.empty((E, 2 * inter, K // 32), np.uint8)
+    ow2 = np.empty((E, H, r2), np.uint8)
+    os2 = np.empty((E, H, inter // 32), np.uint8)
+    rc = lib().orc_moe_copies(elem, E, Np, inter, K, H, _ptr(w13), _ptr(s13), _ptr(w2),
+                              _ptr(s2), _ptr(ow13), _ptr(os13), _ptr(ow2), _ptr(os2))
+    if rc == 1:
+        raise ValueError("the expert padding is not zero")
+    if rc:
+        raise ValueError("bad shape")
+    return ow13, os13, ow2, os2
+
+
+def silu(v: float) -> float:
+    return lib().orc_silu(float(v))
+
+
+def bf16_round(v: float) -> int:
+    return int(lib().orc_bf16_round(float(v)))
+
+
+def bf16_round_array(a: np.ndarray) -> np.ndarray:
+    """Elementwise orc_bf16_round, as uint16 bit patterns."""
+    f = np.vectorize(lambda v: lib().orc_bf16_round(float(v)), otypes=[np.uint16])
+    return f(np.asarray(a, np.float64))
+
+
+def moe_gate_up(elem, E, inter, K, w13, codes, x, ids):
+    """fp64 h [T, topk, inter] = silu(x . gate^T) * (x . up^T) over the
+    interleaved expert rows (gate row i at 2 i, up row i at 2 i + 1)."""
+    w13 = _c(w13, np.uint8)
+    codes = _c(codes, np.uint8)
+    x = _c(x, np.uint16)
+    ids = _c(ids, np.int32)
+    T, topk = ids.shape
+    h = np.empty((T, topk, inter), np.float64)
+    lib().orc_moe_gate_up(elem, E, inter, K, _ptr(w13), _ptr(codes), T, topk, _ptr(x),
+                          x.shape[1], _ptr(ids), _ptr(h))
+    return h
+
+
+def moe_linear_rows(elem, E, N, K, w, codes, a, ids, weights=None):
+    """The grouped linear with one bf16 activation row per slot: a [T*topk, K]
+    (or [T, topk, K]); fp64 per-slot [T, topk, N] or combined [T, N]."""
+    w = _c(w, np.uint8)
+    codes = _c(codes, np.uint8)
+    ids = _c(ids, np.int32)
+    T, topk = ids.shape
+    a = _c(np.asarray(a).reshape(T * topk, -1), np.uint16)
+    weights = _c(weights, np.float32)
+    shape = (T, N) if weights is not None else (T, topk, N)
+    y = np.empty(shape, np.float64)
+    lib().orc_moe_linear_rows(elem, E, N, K, _ptr(w), _ptr(codes), T, topk, _ptr(a),
+                              a.shape[1], _ptr(ids), _ptr(weights), _ptr(y))
     return y
 
 

@@ -30,6 +30,7 @@
  *   R4  K is padded to a multiple of 128 with zero bytes and scale code 128
  *       ([weights942] dense_copy); padding never enters a sum.
  *   R5  MoE ids outside [0, E) give all-zero output rows.
+ *   R18 the gated activation of the MoE up-gate product is SiLU.
  *
  * Parity pins: every function here is checked in tests/test_oracle_*.py
  * against closed forms, brute force and exact rational arithmetic.
@@ -452,6 +453,163 @@ void orc_moe_linear(int elem, int64_t E, int64_t N, int64_t K, const uint8_t *w,
                 if (e >= 0 && e < E)
                     for (kk = 0; kk < K; kk++)
                         s += orc_bf16_value(x[t * ldx + kk]) *
+                             orc_weight(elem, ORC_ROW32, E, N, K, w, codes, e, n, kk);
+                if (weights)
+                    y[t * N + n] += (double)weights[t * topk + k] * s;
+                else
+                    y[(t * topk + k) * N + n] = s;
+            }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* The MoE block around the grouped linear                              */
+/* ------------------------------------------------------------------ */
+
+/* Load-time copies of the expert tensors ([weights942] moe_copies): the
+ * input w13 holds, per expert, 2 Np rows -- the gate rows 0 .. inter - 1,
+ * zero rows up to Np, the up rows Np .. Np + inter - 1, zero rows up to 2 Np
+ * -- of rowb bytes each (K / 2 for e2m1, K for e4m3), with codes
+ * [E, 2 Np, K / 32]; w2 is [E, H, Np] values (bytes per row Np / 2 or Np)
+ * with codes [E, H, Np / 32].  The copies are
+ *   out_w13[e][2 i][:]     = w13[e][i][:]        (gate row i)
+ *   out_w13[e][2 i + 1][:] = w13[e][Np + i][:]   (up row i),   i < inter,
+ * the codes alike, and w2 / its codes cut to the first inter values of each
+ * row.  Returns 1, copying nothing, when a padding byte of the weights is
+ * not zero (the page refuses it), 2 for shapes outside inter <= Np,
+ * inter % 32 == 0, K % 32 == 0.  The gfx942 copy also rewrites -0 nibbles;
+ * this one keeps every byte (-0 decodes equal to +0, reading R7). */
+int orc_moe_copies(int elem, int64_t E, int64_t Np, int64_t inter, int64_t K,
+                   int64_t H, const uint8_t *w13, const uint8_t *s13,
+                   const uint8_t *w2, const uint8_t *s2, uint8_t *out_w13,
+                   uint8_t *out_s13, uint8_t *out_w2, uint8_t *out_s2)
+{
+    const int64_t rowb = elem == ORC_E2M1 ? K / 2 : K;        /* w13 row bytes */
+    const int64_t kb = K / 32;                                  /* w13 codes per row */
+    const int64_t r2in = elem == ORC_E2M1 ? Np / 2 : Np;        /* w2 row bytes in */
+    const int64_t r2out = elem == ORC_E2M1 ? inter / 2 : inter; /* w2 row bytes out */
+    int64_t e, i, g, b, h;
+    if (inter < 1 || inter > Np || inter % 32 != 0 || Np % 32 != 0 || K % 32 != 0)
+        return 2;
+    for (e = 0; e < E; e++) {
+        for (g = 0; g < 2; g++)
+            for (i = inter; i < Np; i++)
+                for (b = 0; b < rowb; b++)
+                    if (w13[(e * 2 * Np + g * Np + i) * rowb + b] != 0)
+                        return 1;
+        for (h = 0; h < H; h++)
+            for (b = r2out; b < r2in; b++)
+                if (w2[(e * H + h) * r2in + b] != 0)
+                    return 1;
+    }
+    for (e = 0; e < E; e++) {
+        for (i = 0; i < inter; i++)
+            for (g = 0; g < 2; g++) {
+                const int64_t src = e * 2 * Np + g * Np + i, dst = e * 2 * inter + 2 * i + g;
+                memcpy(out_w13 + dst * rowb, w13 + src * rowb, (size_t)rowb);
+                memcpy(out_s13 + dst * kb, s13 + src * kb, (size_t)kb);
+            }
+        for (h = 0; h < H; h++) {
+            memcpy(out_w2 + (e * H + h) * r2out, w2 + (e * H + h) * r2in, (size_t)r2out);
+            memcpy(out_s2 + (e * H + h) * (inter / 32), s2 + (e * H + h) * (Np / 32),
+                   (size_t)(inter / 32));
+        }
+    }
+    return 0;
+}
+
+/* SiLU, v * sigmoid(v) = v / (1 + e^-v), in binary64.  The pages pair each
+ * gate row with its up row (moe_copies) for the routed experts' up-gate
+ * product; the gated activation they feed is read as SiLU, the activation of
+ * the DeepSeek-family MoE these pages belong to (reading R18). */
+double orc_silu(double v)
+{
+    return v / (1.0 + exp(-v));
+}
+
+/* Round a binary64 value to the nearest bf16 (ties to even), as bits.  The
+ * MoE block hands its hidden activation h on in the activation dtype, bf16
+ * ([rocm_native] apply_weights: outputs in the input dtype).  bf16 has 8
+ * significant bits and binary32's exponent range: a value in [2^(x-1), 2^x)
+ * lies on the grid 2^(x-8); below 2^-126 the grid is 2^-133 (subnormals). */
+uint16_t orc_bf16_round(double v)
+{
+    const uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v), step, q, r, res;
+    float f;
+    uint32_t u;
+    int x;
+    if (isnan(v))
+        return 0x7FC0;
+    if (a == 0.0)
+        return sign;
+    frexp(a, &x);                              /* a in [2^(x-1), 2^x) */
+    step = x - 1 >= -126 ? ldexp(1.0, x - 8) : ldexp(1.0, -133);
+    q = a / step;                              /* exact: step is a power of two */
+    r = floor(q);
+    if (q - r > 0.5 || (q - r == 0.5 && fmod(r, 2.0) != 0.0))
+        r += 1.0;
+    res = r * step;
+    if (res > 3.3895313892515355e38)           /* above the largest bf16: Inf */
+        return sign | 0x7F80;
+    f = (float)res;                            /* exact: res is on the bf16 grid */
+    memcpy(&u, &f, 4);
+    return sign | (uint16_t)(u >> 16);
+}
+
+/* The up-gate product of the routed experts over the interleaved copies:
+ * for every token t, slot k with expert e = ids[t][k] in [0, E), and i < inter,
+ *   g = x[t] . Wf[e][2 i]^T,  u = x[t] . Wf[e][2 i + 1]^T   (binary64 sums),
+ *   h[t][k][i] = silu(g) * u;
+ * zero rows for ids outside [0, E) (R5).  w13: [E, 2 inter, K(/2)] standard
+ * layout with ROW32 codes [E 2 inter, K / 32]. */
+void orc_moe_gate_up(int elem, int64_t E, int64_t inter, int64_t K, const uint8_t *w13,
+                     const uint8_t *codes, int64_t T, int64_t topk, const uint16_t *x,
+                     int64_t ldx, const int32_t *ids, double *h)
+{
+    const int64_t N = 2 * inter;
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < inter; i++) {
+        int64_t t, k, kk;
+        for (t = 0; t < T; t++)
+            for (k = 0; k < topk; k++) {
+                const int32_t e = ids[t * topk + k];
+                double g = 0.0, u = 0.0;
+                if (e >= 0 && e < E)
+                    for (kk = 0; kk < K; kk++) {
+                        const double a = orc_bf16_value(x[t * ldx + kk]);
+                        g += a * orc_weight(elem, ORC_ROW32, E, N, K, w13, codes, e, 2 * i, kk);
+                        u += a * orc_weight(elem, ORC_ROW32, E, N, K, w13, codes, e, 2 * i + 1, kk);
+                    }
+                h[(t * topk + k) * inter + i] = (e >= 0 && e < E) ? orc_silu(g) * u : 0.0;
+            }
+    }
+}
+
+/* The grouped linear with one activation row per routed slot (the down
+ * projection of the MoE block reads the hidden row h[t][k] of its slot):
+ *   y[t][k][:] = a[t topk + k] . Wf[ids[t][k]]^T             (per slot), or
+ *   out[t][:]  = sum_k weight[t][k] y[t][k][:], k ascending  (combined),
+ * binary64, zero rows for ids outside [0, E).  a: bf16 [T topk, lda]. */
+void orc_moe_linear_rows(int elem, int64_t E, int64_t N, int64_t K, const uint8_t *w,
+                         const uint8_t *codes, int64_t T, int64_t topk,
+                         const uint16_t *a, int64_t lda, const int32_t *ids,
+                         const float *weights, double *y)
+{
+    int64_t n;
+    int64_t rows = weights ? T : T * topk;
+    memset(y, 0, sizeof(double) * (size_t)(rows * N));
+#pragma omp parallel for schedule(static)
+    for (n = 0; n < N; n++) {
+        int64_t t, k, kk;
+        for (t = 0; t < T; t++)
+            for (k = 0; k < topk; k++) {
+                int32_t e = ids[t * topk + k];
+                double s = 0.0;
+                if (e >= 0 && e < E)
+                    for (kk = 0; kk < K; kk++)
+                        s += orc_bf16_value(a[(t * topk + k) * lda + kk]) *
                              orc_weight(elem, ORC_ROW32, E, N, K, w, codes, e, n, kk);
                 if (weights)
                     y[t * N + n] += (double)weights[t * topk + k] * s;
