@@ -223,6 +223,63 @@ mx_status mx_moe_linear(int elem, int64_t E, int64_t N, int64_t K,
                         void *y, void *ws, size_t ws_bytes,
                         mx_stream_t stream);
 
+/* ---- The MoE block around the grouped linear ---- */
+
+/* Load-time expert copies ([weights942] moe_copies).  Input, as a model's
+ * checkpoint holds the MoE experts (standard layouts, elem E2M1 or E4M3):
+ *   w13 (device) [E, 2 Np, rowb] bytes, rowb = K/2 (E2M1) or K (E4M3): gate
+ *       rows 0 .. inter-1, zero rows to Np, up rows Np .. Np+inter-1, zero
+ *       rows to 2 Np;  s13 (device) codes [E, 2 Np, K/32];
+ *   w2  (device) [E, H, Np values] (Np/2 or Np bytes a row), zero beyond
+ *       inter;  s2 (device) codes [E, H, Np/32].
+ * Output (device, caller-owned, 16-byte aligned):
+ *   w13_out [E, 2 inter, rowb] with gate row i at 2 i and up row i at 2 i + 1,
+ *   s13_out [E, 2 inter, K/32] alike, w2_out [E, H, inter values],
+ *   s2_out [E, H, inter/32].
+ * Bytes are copied verbatim (-0 nibbles kept).  Then pack them with
+ * mx_pack_weights(elem, ROW32, E, 2 inter, K, ...) and
+ * mx_pack_weights(elem, ROW32, E, H, inter, ...).
+ * Rules: inter % 32 == 0, Np % 32 == 0, inter <= Np, K % 32 == 0, E, H >= 1;
+ *   ws (device) at least 256 bytes of scratch.
+ * Errors: MX_ERR_VALUE (nothing copied) when a padding byte of w13 or w2 is
+ *   not zero, as the page refuses it.  Load-time: the call reads the padding
+ *   check back and synchronizes `stream`. */
+mx_status mx_moe_copies(int elem, int64_t E, int64_t Np, int64_t inter, int64_t K,
+                        int64_t H, const void *w13, const void *s13, const void *w2,
+                        const void *s2, void *w13_out, void *s13_out, void *w2_out,
+                        void *s2_out, void *ws, size_t ws_bytes, mx_stream_t stream);
+
+/* Up-gate product of the routed experts with the gated activation fused
+ * ([weights942] moe_copies pairs each gate row with its up row; the
+ * activation is read as SiLU):
+ *   h[t k][i] = silu(x[t] . gate_e[i]^T) * (x[t] . up_e[i]^T),  e = id[t][k],
+ * fp32 accumulation, silu in fp32, one bf16 rounding.
+ *   w13_packed, codes_packed (device): mx_pack_weights(elem, ROW32, E,
+ *       2 inter, K) of mx_moe_copies' w13_out / s13_out
+ *   x (device) bf16 [T, ldx] as in mx_moe_linear
+ *   h (device) bf16 [T topk, ldh], 16-byte aligned, ldh % 8 == 0, ldh >= inter;
+ *       a slot whose id is outside [0, E) gets a zero row
+ * Rules as mx_moe_linear, with N = 2 inter (inter % 8 == 0). */
+mx_status mx_moe_gate_up(int elem, int64_t E, int64_t inter, int64_t K,
+                         const void *w13_packed, const void *codes_packed,
+                         int64_t T, int64_t topk, const void *x, int64_t ldx,
+                         const int32_t *topk_ids, void *h, int64_t ldh,
+                         mx_stream_t stream);
+
+/* Down projection of the routed experts on the per-slot hidden rows:
+ *   per slot: y[t][k][:] = h[t topk + k] . W2_e^T,  e = id[t][k];
+ *   combined (topk_weights != NULL): y[t][:] = sum_k w[t][k] y_slot[t][k][:]
+ * (as mx_moe_linear, whose workspace rule applies: mx_moe_workspace(elem, E,
+ * H, inter, T, topk, combine)).
+ *   w2_packed, codes_packed (device): mx_pack_weights(elem, ROW32, E, H,
+ *       inter) of mx_moe_copies' w2_out / s2_out
+ *   h (device) bf16 [T topk, ldh] (mx_moe_gate_up's output) */
+mx_status mx_moe_down(int elem, int64_t E, int64_t H, int64_t inter,
+                      const void *w2_packed, const void *codes_packed,
+                      int64_t T, int64_t topk, const void *h, int64_t ldh,
+                      const int32_t *topk_ids, const float *topk_weights,
+                      void *y, void *ws, size_t ws_bytes, mx_stream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char *mx_status_str(mx_status status);
 

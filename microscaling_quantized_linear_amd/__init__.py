@@ -22,7 +22,8 @@ __all__ = [
     "MX_RULE_CEIL448", "MX_ACT_BF16", "MX_ACT_MXFP8", "MX_ACT_MXFP8_T16", "MXError", "lib",
     "mx_packed_sizes", "mx_pack_weights", "mx_quant_act", "mx_act_t16_sizes",
     "mx_quant_act_t16", "mx_linear_workspace",
-    "mx_linear", "mx_moe_workspace", "mx_moe_linear", "mx_status_str",
+    "mx_linear", "mx_moe_workspace", "mx_moe_linear", "mx_moe_copies", "mx_moe_gate_up",
+    "mx_moe_down", "mx_status_str",
     "mx_arch_supported",
 ]
 
@@ -66,9 +67,14 @@ def lib() -> C.CDLL:
         L.mx_moe_workspace.argtypes = [i32, i64, i64, i64, i64, i64, i32, C.POINTER(sz)]
         L.mx_moe_linear.argtypes = [i32, i64, i64, i64, p, p, i64, i64, p, i64, p, p, p,
                                     p, sz, p]
+        L.mx_moe_copies.argtypes = [i32, i64, i64, i64, i64, i64, p, p, p, p, p, p, p, p, p,
+                                    sz, p]
+        L.mx_moe_gate_up.argtypes = [i32, i64, i64, i64, p, p, i64, i64, p, i64, p, p, i64, p]
+        L.mx_moe_down.argtypes = [i32, i64, i64, i64, p, p, i64, i64, p, i64, p, p, p, p, sz,
+                                  p]
         for name in ("mx_packed_sizes", "mx_pack_weights", "mx_quant_act", "mx_act_t16_sizes",
                      "mx_quant_act_t16", "mx_linear_workspace", "mx_linear", "mx_moe_workspace",
-                     "mx_moe_linear"):
+                     "mx_moe_linear", "mx_moe_copies", "mx_moe_gate_up", "mx_moe_down"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -160,3 +166,25 @@ def mx_moe_linear(elem, E, N, K, w_packed, codes_packed, T, topk, x, ldx, topk_i
     _check(lib().mx_moe_linear(elem, E, N, K, _ptr(w_packed), _ptr(codes_packed), T, topk,
                                _ptr(x), ldx, _ptr(topk_ids), _ptr(topk_weights), _ptr(y),
                                _ptr(ws), ws_bytes, _stream(stream)), "mx_moe_linear")
+
+
+def mx_moe_copies(elem, E, Np, inter, K, H, w13, s13, w2, s2, w13_out, s13_out, w2_out, s2_out,
+                  ws, ws_bytes, stream=None):
+    _check(lib().mx_moe_copies(elem, E, Np, inter, K, H, _ptr(w13), _ptr(s13), _ptr(w2),
+                               _ptr(s2), _ptr(w13_out), _ptr(s13_out), _ptr(w2_out),
+                               _ptr(s2_out), _ptr(ws), ws_bytes, _stream(stream)),
+           "mx_moe_copies")
+
+
+def mx_moe_gate_up(elem, E, inter, K, w13_packed, codes_packed, T, topk, x, ldx, topk_ids, h,
+                   ldh, stream=None):
+    _check(lib().mx_moe_gate_up(elem, E, inter, K, _ptr(w13_packed), _ptr(codes_packed), T,
+                                topk, _ptr(x), ldx, _ptr(topk_ids), _ptr(h), ldh,
+                                _stream(stream)), "mx_moe_gate_up")
+
+
+def mx_moe_down(elem, E, H, inter, w2_packed, codes_packed, T, topk, h, ldh, topk_ids,
+                topk_weights, y, ws, ws_bytes, stream=None):
+    _check(lib().mx_moe_down(elem, E, H, inter, _ptr(w2_packed), _ptr(codes_packed), T, topk,
+                             _ptr(h), ldh, _ptr(topk_ids), _ptr(topk_weights), _ptr(y),
+                             _ptr(ws), ws_bytes, _stream(stream)), "mx_moe_down")

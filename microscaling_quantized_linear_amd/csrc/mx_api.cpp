@@ -115,6 +115,55 @@ mx::GemvShape gemv_shape(int64_t S, bool moe) {
     return g;
 }
 
+// The grouped MoE GEMV behind mx_moe_linear, mx_moe_gate_up and mx_moe_down:
+// xslot reads activation row i for pair i (else its token's row), epi writes
+// silu(row 2 i) * row 2 i + 1 as output i (width N / 2, per slot only).
+mx_status moe_run(int elem, int64_t E, int64_t N, int64_t K, const void *w_packed,
+                  const void *codes_packed, int64_t T, int64_t topk, const void *x, int64_t ldx,
+                  bool xslot, bool epi, const int32_t *topk_ids, const float *topk_weights,
+                  void *y, int64_t ldy, void *ws, size_t ws_bytes, mx_stream_t stream) {
+    size_t need = 0;
+    mx_status st = mx_moe_workspace(elem, E, N, K, T, topk, topk_weights ? 1 : 0, &need);
+    if (st != MX_OK) return st;
+    const int64_t xrows = xslot ? T * topk : T;
+    if (ldx < K) return MX_ERR_SHAPE;
+    if (xrows * ldx * 2 > kMaxRsrc) return MX_ERR_SHAPE;
+    if (!w_packed || !codes_packed || !x || !topk_ids || !y) return MX_ERR_NULL;
+    if (!aligned16(w_packed) || !aligned16(codes_packed) || !aligned16(x) || !aligned16(y) ||
+        ldx % 8 != 0 || (reinterpret_cast<uintptr_t>(topk_ids) & 3u) ||
+        (topk_weights && (reinterpret_cast<uintptr_t>(topk_weights) & 3u)))
+        return MX_ERR_ALIGN;
+    if (need > 0 && (!ws || ws_bytes < need)) return MX_ERR_WORKSPACE;
+    if (need > 0 && !aligned16(ws)) return MX_ERR_ALIGN;
+    if ((st = device_ok()) != MX_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const int64_t Kp = padded_k(K);
+    mx::GemvArgs a{};
+    a.w = static_cast<const uint8_t *>(w_packed);
+    a.codes = static_cast<const uint8_t *>(codes_packed);
+    a.E = E;
+    a.N = N;
+    a.K = K;
+    a.rows = T;
+    a.topk = topk;
+    a.xrows = xrows;
+    a.x = x;
+    a.ldx = ldx;
+    a.ids = topk_ids;
+    a.y = static_cast<uint16_t *>(y);
+    a.ldy = ldy;
+    a.xslot = xslot ? 1 : 0;
+    a.epi = epi ? 1 : 0;
+    float *slots = topk_weights ? static_cast<float *>(ws) : nullptr;
+    a.ws = slots;
+    if ((st = launched(mx::launch_gemv(elem, ROW32, ACT_BF16, true, a,
+                                       gemv_shape(Kp / 128, true), s))) != MX_OK)
+        return st;
+    if (topk_weights)
+        return launched(mx::launch_moe_combine(T, topk, N, slots, topk_weights, y, s));
+    return MX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -393,43 +442,58 @@ mx_status mx_moe_linear(int elem, int64_t E, int64_t N, int64_t K, const void *w
                         const void *codes_packed, int64_t T, int64_t topk, const void *x,
                         int64_t ldx, const int32_t *topk_ids, const float *topk_weights, void *y,
                         void *ws, size_t ws_bytes, mx_stream_t stream) {
-    size_t need = 0;
-    mx_status st = mx_moe_workspace(elem, E, N, K, T, topk, topk_weights ? 1 : 0, &need);
-    if (st != MX_OK) return st;
-    if (ldx < K) return MX_ERR_SHAPE;
-    if (T * ldx * 2 > kMaxRsrc) return MX_ERR_SHAPE;
-    if (!w_packed || !codes_packed || !x || !topk_ids || !y) return MX_ERR_NULL;
-    if (!aligned16(w_packed) || !aligned16(codes_packed) || !aligned16(x) || !aligned16(y) ||
-        ldx % 8 != 0 || (reinterpret_cast<uintptr_t>(topk_ids) & 3u) ||
-        (topk_weights && (reinterpret_cast<uintptr_t>(topk_weights) & 3u)))
+    return moe_run(elem, E, N, K, w_packed, codes_packed, T, topk, x, ldx, false, false,
+                   topk_ids, topk_weights, y, N, ws, ws_bytes, stream);
+}
+
+mx_status mx_moe_copies(int elem, int64_t E, int64_t Np, int64_t inter, int64_t K, int64_t H,
+                        const void *w13, const void *s13, const void *w2, const void *s2,
+                        void *w13_out, void *s13_out, void *w2_out, void *s2_out, void *ws,
+                        size_t ws_bytes, mx_stream_t stream) {
+    if (elem != E4M3 && elem != E2M1) return MX_ERR_UNSUPPORTED;
+    if (E < 1 || H < 1 || inter < 32 || inter % 32 != 0 || Np % 32 != 0 || inter > Np ||
+        K < 32 || K % 32 != 0)
+        return MX_ERR_SHAPE;
+    if (!w13 || !s13 || !w2 || !s2 || !w13_out || !s13_out || !w2_out || !s2_out || !ws)
+        return MX_ERR_NULL;
+    if (!aligned16(w13) || !aligned16(w2) || !aligned16(w13_out) || !aligned16(w2_out) ||
+        !aligned16(ws))
         return MX_ERR_ALIGN;
-    if (need > 0 && (!ws || ws_bytes < need)) return MX_ERR_WORKSPACE;
-    if (need > 0 && !aligned16(ws)) return MX_ERR_ALIGN;
-    if ((st = device_ok()) != MX_OK) return st;
+    if (ws_bytes < 256) return MX_ERR_WORKSPACE;
+    mx_status st = device_ok();
+    if (st != MX_OK) return st;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const int64_t Kp = padded_k(K);
-    mx::GemvArgs a{};
-    a.w = static_cast<const uint8_t *>(w_packed);
-    a.codes = static_cast<const uint8_t *>(codes_packed);
-    a.E = E;
-    a.N = N;
-    a.K = K;
-    a.rows = T;
-    a.topk = topk;
-    a.xrows = T;
-    a.x = x;
-    a.ldx = ldx;
-    a.ids = topk_ids;
-    a.y = static_cast<uint16_t *>(y);
-    a.ldy = N;
-    float *slots = topk_weights ? static_cast<float *>(ws) : nullptr;
-    a.ws = slots;
-    if ((st = launched(mx::launch_gemv(elem, ROW32, ACT_BF16, true, a,
-                                       gemv_shape(Kp / 128, true), s))) != MX_OK)
+    int *bad = static_cast<int *>(ws);
+    if (hipMemsetAsync(bad, 0, sizeof(int), s) != hipSuccess) return MX_ERR_LAUNCH;
+    if ((st = launched(mx::launch_moe_padding_check(elem, E, Np, inter, K, H, w13, w2, bad, s))) !=
+        MX_OK)
         return st;
-    if (topk_weights)
-        return launched(mx::launch_moe_combine(T, topk, N, slots, topk_weights, y, s));
-    return MX_OK;
+    int h = 0;
+    if (hipMemcpyAsync(&h, bad, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return MX_ERR_LAUNCH;
+    if (h) return MX_ERR_VALUE;
+    return launched(mx::launch_moe_copies(elem, E, Np, inter, K, H, w13, s13, w2, s2, w13_out,
+                                          s13_out, w2_out, s2_out, s));
+}
+
+mx_status mx_moe_gate_up(int elem, int64_t E, int64_t inter, int64_t K, const void *w13_packed,
+                         const void *codes_packed, int64_t T, int64_t topk, const void *x,
+                         int64_t ldx, const int32_t *topk_ids, void *h, int64_t ldh,
+                         mx_stream_t stream) {
+    if (inter < 8 || inter % 8 != 0) return MX_ERR_SHAPE;
+    if (ldh < inter) return MX_ERR_SHAPE;
+    if (ldh % 8 != 0) return MX_ERR_ALIGN;
+    return moe_run(elem, E, 2 * inter, K, w13_packed, codes_packed, T, topk, x, ldx, false, true,
+                   topk_ids, nullptr, h, ldh, nullptr, 0, stream);
+}
+
+mx_status mx_moe_down(int elem, int64_t E, int64_t H, int64_t inter, const void *w2_packed,
+                      const void *codes_packed, int64_t T, int64_t topk, const void *h,
+                      int64_t ldh, const int32_t *topk_ids, const float *topk_weights, void *y,
+                      void *ws, size_t ws_bytes, mx_stream_t stream) {
+    return moe_run(elem, E, H, inter, w2_packed, codes_packed, T, topk, h, ldh, true, false,
+                   topk_ids, topk_weights, y, H, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

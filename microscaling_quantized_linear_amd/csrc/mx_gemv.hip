@@ -22,7 +22,11 @@
 //
 // Grouped MoE: a workgroup first collects the (token, slot) pairs routed to
 // its expert with a wavefront ballot (in pair order) and exits before reading
-// any weight byte if there are none.
+// any weight byte if there are none.  Two runtime modes serve the MoE block:
+// `xslot` reads one activation row per slot (the down projection of the
+// hidden rows), `epi` turns interleaved (gate, up) row pairs into
+// silu(gate) * up, one output per pair ([weights942] moe_copies pairs gate
+// row i with up row i at rows 2 i, 2 i + 1).
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -80,9 +84,11 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
         nslots = nslots_sh;
         if (nslots == 0) return;                     // no token: no weight bytes read
         if (e == p.E) {                              // out-of-range ids: zero rows
-            for (int64_t idx = threadIdx.x; idx < nslots * 16 * ntiles; idx += NW * 64) {
-                const int64_t pair = slots[idx / (16 * ntiles)];
-                const int64_t n = 16 * t0 + idx % (16 * ntiles);
+            // (with the SiLU epilogue a 16-row tile gives 8 outputs)
+            const int64_t per = p.epi ? 8 : 16;
+            for (int64_t idx = threadIdx.x; idx < nslots * per * ntiles; idx += NW * 64) {
+                const int64_t pair = slots[idx / (per * ntiles)];
+                const int64_t n = per * t0 + idx % (per * ntiles);
                 if (p.ws)
                     p.ws[pair * p.N + n] = 0.f;
                 else
@@ -134,7 +140,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
         if (slot < nslots) {
             if (MOE) {
                 const int64_t pair = slots[slot];
-                xrow = pair / p.topk;
+                xrow = p.xslot ? pair : pair / p.topk;    // one activation row per slot, or per token
                 yrow = pair;
             } else {
                 xrow = slot;
@@ -293,7 +299,14 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
                 // lane (r, j) holds rows 4 j .. 4 j + 3 of tile t0 + g for slot r
                 const int64_t n0 = 16 * (t0 + g) + 4 * j;
                 const v4f a = acc[g];
-                if (p.ws) {
+                if (MOE && p.epi) {
+                    // rows 4 j .. 4 j + 3 are (gate, up) of outputs n0 / 2 and
+                    // n0 / 2 + 1 (interleaved copies): silu(gate) * up
+                    const float h0 = a[0] / (1.f + __expf(-a[0])) * a[1];
+                    const float h1 = a[2] / (1.f + __expf(-a[2])) * a[3];
+                    *reinterpret_cast<uint32_t *>(p.y + yrow * p.ldy + n0 / 2) =
+                        bf16_bits(h0) | (bf16_bits(h1) << 16);
+                } else if (p.ws) {
                     *reinterpret_cast<v4f *>(p.ws + yrow * p.N + n0) = a;
                 } else {
                     float v[4] = {a[0], a[1], a[2], a[3]};

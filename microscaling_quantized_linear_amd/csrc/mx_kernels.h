@@ -31,6 +31,8 @@ struct GemvArgs {
     uint16_t *y;             // bf16 output
     int64_t ldy;
     float *ws;               // MoE combine mode: fp32 per-slot rows [T*topk, N]
+    int xslot;               // MoE: activation row of pair i is i (else i / topk)
+    int epi;                 // MoE: 1 = silu(row 2i) * row 2i+1 -> output i (width N / 2)
 };
 
 struct GemmArgs {
@@ -56,6 +58,14 @@ hipError_t launch_act_data_t16(int64_t M, int64_t K, const void *xq, int64_t ldq
 
 hipError_t launch_pack(int elem, int layout, int64_t E, int64_t N, int64_t K, const void *w,
                        const void *codes, void *wp, void *cp, int *bad, hipStream_t stream);
+// [weights942] moe_copies: the padding check (sets *bad), then the copies
+hipError_t launch_moe_padding_check(int elem, int64_t E, int64_t Np, int64_t inter, int64_t K,
+                                    int64_t H, const void *w13, const void *w2, int *bad,
+                                    hipStream_t stream);
+hipError_t launch_moe_copies(int elem, int64_t E, int64_t Np, int64_t inter, int64_t K,
+                             int64_t H, const void *w13, const void *s13, const void *w2,
+                             const void *s2, void *ow13, void *os13, void *ow2, void *os2,
+                             hipStream_t stream);
 hipError_t launch_quant(int64_t M, int64_t K, const void *x, int64_t ldx, void *xq, int64_t ldq,
                         void *xcodes, int64_t ldc, int rule, hipStream_t stream);
 // Launch shape of the GEMV: nw wavefronts per workgroup (1, 2, 4, 8) split

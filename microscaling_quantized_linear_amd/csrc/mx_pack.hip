@@ -159,4 +159,114 @@ hipError_t launch_pack(int elem, int layout, int64_t E, int64_t N, int64_t K, co
     return hipGetLastError();
 }
 
+// ---- expert copies for the MoE block ([weights942] moe_copies) ----
+// w13 [E, 2 Np, rowb]: gate rows 0 .. inter - 1, zero rows to Np, up rows
+// Np .. Np + inter - 1, zero rows to 2 Np.  Copies: row 2 i <- gate row i,
+// row 2 i + 1 <- up row i; w2 [E, H, Np values] cut to inter values.  rowb,
+// the w2 row bytes and their padding are multiples of 16 (K, inter, Np are
+// multiples of 32), so everything but the codes moves in 16-byte pieces.
+
+// one 16-byte piece of padding per thread: w13's zero rows, then w2's zero
+// columns; any non-zero byte sets *bad
+__global__ void __launch_bounds__(256) moe_padding_kernel(
+    const v4u *__restrict__ w13, const v4u *__restrict__ w2, int64_t E, int64_t Np,
+    int64_t inter, int64_t rowb16, int64_t r2in16, int64_t r2out16, int64_t H,
+    int *__restrict__ bad) {
+    const int64_t pad13 = E * 2 * (Np - inter) * rowb16;   // pieces in w13's padding rows
+    const int64_t pad2 = E * H * (r2in16 - r2out16);       // pieces in w2's padding columns
+    bool found = false;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < pad13 + pad2;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        v4u v;
+        if (q < pad13) {
+            const int64_t b = q % rowb16, row = q / rowb16;
+            const int64_t per = 2 * (Np - inter), e = row / per, pr = row % per;
+            const int64_t src = e * 2 * Np + (pr < Np - inter ? inter + pr : Np + inter + (pr - (Np - inter)));
+            v = w13[src * rowb16 + b];
+        } else {
+            const int64_t q2 = q - pad13, w = r2in16 - r2out16;
+            v = w2[(q2 / w) * r2in16 + r2out16 + q2 % w];
+        }
+        found |= (v[0] | v[1] | v[2] | v[3]) != 0u;
+    }
+    if (found) atomicOr(bad, 1);
+}
+
+__global__ void __launch_bounds__(256) moe_copy_kernel(
+    const v4u *__restrict__ w13, const v4u *__restrict__ w2, v4u *__restrict__ ow13,
+    v4u *__restrict__ ow2, int64_t E, int64_t Np, int64_t inter, int64_t rowb16,
+    int64_t r2in16, int64_t r2out16, int64_t H) {
+    const int64_t n13 = E * 2 * inter * rowb16, n2 = E * H * r2out16;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n13 + n2;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        if (q < n13) {
+            const int64_t b = q % rowb16, row = q / rowb16;    // output row e 2 inter + 2 i + g
+            const int64_t e = row / (2 * inter), rr = row % (2 * inter);
+            const int64_t src = e * 2 * Np + (rr % 2) * Np + rr / 2;
+            ow13[q] = w13[src * rowb16 + b];
+        } else {
+            const int64_t q2 = q - n13;
+            ow2[q2] = w2[(q2 / r2out16) * r2in16 + q2 % r2out16];
+        }
+    }
+}
+
+// the codes, one byte per thread: s13 [E, 2 Np, kb] interleaved like the
+// rows, s2 [E, H, Np / 32] cut to inter / 32
+__global__ void __launch_bounds__(256) moe_copy_codes_kernel(
+    const uint8_t *__restrict__ s13, const uint8_t *__restrict__ s2, uint8_t *__restrict__ os13,
+    uint8_t *__restrict__ os2, int64_t E, int64_t Np, int64_t inter, int64_t kb, int64_t H) {
+    const int64_t n13 = E * 2 * inter * kb, c2in = Np / 32, c2out = inter / 32;
+    const int64_t n2 = E * H * c2out;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n13 + n2;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        if (q < n13) {
+            const int64_t b = q % kb, row = q / kb;
+            const int64_t e = row / (2 * inter), rr = row % (2 * inter);
+            os13[q] = s13[(e * 2 * Np + (rr % 2) * Np + rr / 2) * kb + b];
+        } else {
+            const int64_t q2 = q - n13;
+            os2[q2] = s2[(q2 / c2out) * c2in + q2 % c2out];
+        }
+    }
+}
+
+static unsigned grid_for(int64_t n) {
+    const int64_t g = (n + 255) / 256;
+    return (unsigned)(g < 1 ? 1 : (g > 65536 ? 65536 : g));
+}
+
+hipError_t launch_moe_padding_check(int elem, int64_t E, int64_t Np, int64_t inter, int64_t K,
+                                    int64_t H, const void *w13, const void *w2, int *bad,
+                                    hipStream_t st) {
+    const int64_t rowb16 = (elem == E2M1 ? K / 2 : K) / 16;
+    const int64_t r2in16 = (elem == E2M1 ? Np / 2 : Np) / 16;
+    const int64_t r2out16 = (elem == E2M1 ? inter / 2 : inter) / 16;
+    const int64_t n = E * 2 * (Np - inter) * rowb16 + E * H * (r2in16 - r2out16);
+    hipLaunchKernelGGL(moe_padding_kernel, dim3(grid_for(n)), dim3(256), 0, st,
+                       (const v4u *)w13, (const v4u *)w2, E, Np, inter, rowb16, r2in16,
+                       r2out16, H, bad);
+    return hipGetLastError();
+}
+
+hipError_t launch_moe_copies(int elem, int64_t E, int64_t Np, int64_t inter, int64_t K,
+                             int64_t H, const void *w13, const void *s13, const void *w2,
+                             const void *s2, void *ow13, void *os13, void *ow2, void *os2,
+                             hipStream_t st) {
+    const int64_t rowb16 = (elem == E2M1 ? K / 2 : K) / 16;
+    const int64_t r2in16 = (elem == E2M1 ? Np / 2 : Np) / 16;
+    const int64_t r2out16 = (elem == E2M1 ? inter / 2 : inter) / 16;
+    const int64_t n = E * 2 * inter * rowb16 + E * H * r2out16;
+    hipLaunchKernelGGL(moe_copy_kernel, dim3(grid_for(n)), dim3(256), 0, st, (const v4u *)w13,
+                       (const v4u *)w2, (v4u *)ow13, (v4u *)ow2, E, Np, inter, rowb16, r2in16,
+                       r2out16, H);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nc = E * 2 * inter * (K / 32) + E * H * (inter / 32);
+    hipLaunchKernelGGL(moe_copy_codes_kernel, dim3(grid_for(nc)), dim3(256), 0, st,
+                       (const uint8_t *)s13, (const uint8_t *)s2, (uint8_t *)os13, (uint8_t *)os2,
+                       E, Np, inter, K / 32, H);
+    return hipGetLastError();
+}
+
 }  // namespace mx

@@ -135,8 +135,12 @@ def assert_close(y_bits: np.ndarray, ref: np.ndarray, what: str = ""):
     Where the exact result rounded once to bf16 does not itself reach the
     2e-3 bar (cases with few outputs: the rounding floor of the relative L2
     is then >= 1.9e-3), the relative-L2 test is replaced by a per-element one:
-    every output within one bf16 ulp of the exact result, i.e. the correctly
-    rounded value or its neighbour."""
+    every output within one bf16 ulp of the exact result (the correctly
+    rounded value or its neighbour), or within 2^-12 of its row's largest
+    magnitude -- for outputs whose accuracy is set by the fp32 accumulation of
+    their inputs rather than by the output rounding (tiny values, e.g. SiLU of
+    a very negative gate, where e^g amplifies the gate's absolute error); the
+    contract's own per-element bound is 1e-2 of the row's largest magnitude."""
     y = bf16_to_f64(y_bits).reshape(ref.shape)
     assert np.all(np.isfinite(y)), f"{what}: non-finite output"
     err = y - ref
@@ -145,7 +149,9 @@ def assert_close(y_bits: np.ndarray, ref: np.ndarray, what: str = ""):
     if rel > REL_L2:
         floor = rounding_floor(ref)
         assert floor >= 0.95 * REL_L2, f"{what}: relative L2 {rel:.3e} > {REL_L2} (floor {floor:.3e})"
-        far = np.abs(err) > bf16_ulp(ref)
+        rowmax1 = np.abs(ref.reshape(-1, ref.shape[-1])).max(axis=1, keepdims=True)
+        noise = np.broadcast_to(rowmax1, ref.reshape(-1, ref.shape[-1]).shape).reshape(ref.shape)
+        far = np.abs(err) > np.maximum(bf16_ulp(ref), 2.0 ** -12 * noise)
         assert not far.any(), f"{what}: {far.sum()} outputs more than one bf16 ulp off"
     r2 = ref.reshape(-1, ref.shape[-1])
     e2 = np.abs(err.reshape(-1, ref.shape[-1]))
@@ -153,3 +159,39 @@ def assert_close(y_bits: np.ndarray, ref: np.ndarray, what: str = ""):
     bad = e2 > ROW_FRAC * rowmax
     assert not bad.any(), f"{what}: {bad.sum()} elements beyond 1e-2 * row max"
     return rel
+
+
+def moe_copies(elem, E, Np, inter, K, H, w13, s13, w2, s2):
+    """mx_moe_copies of host arrays: the four outputs as host arrays."""
+    rowb = K // 2 if elem == 1 else K
+    r2 = inter // 2 if elem == 1 else inter
+    outs = [torch.full(shape, 0xAB, dtype=torch.uint8, device=DEV)
+            for shape in ((E, 2 * inter, rowb), (E, 2 * inter, K // 32), (E, H, r2),
+                          (E, H, inter // 32))]
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    mx.mx_moe_copies(elem, E, Np, inter, K, H, dev(w13), dev(s13), dev(w2), dev(s2), *outs, ws,
+                     256)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in outs]
+
+
+def moe_gate_up(elem, E, inter, K, wp, cp, x, ids, ldh=None):
+    T, topk = ids.shape
+    ldh = ldh or inter
+    h = torch.full((T * topk, ldh), 0x7FC0, dtype=torch.int16, device=DEV)
+    mx.mx_moe_gate_up(elem, E, inter, K, wp, cp, T, topk, dev(x), x.shape[1], dev(ids), h, ldh)
+    torch.cuda.synchronize()
+    return host_u16(h)[:, :inter]
+
+
+def moe_down(elem, E, H, inter, wp, cp, h, ids, weights=None):
+    T, topk = ids.shape
+    combine = weights is not None
+    y = torch.empty((T, H) if combine else (T, topk, H), dtype=torch.int16, device=DEV)
+    need = mx.mx_moe_workspace(elem, E, H, inter, T, topk, combine)
+    ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=DEV)
+    hd = dev(np.ascontiguousarray(h.reshape(T * topk, -1)))
+    mx.mx_moe_down(elem, E, H, inter, wp, cp, T, topk, hd, hd.shape[1], dev(ids),
+                   dev(weights) if combine else None, y, ws, need)
+    torch.cuda.synchronize()
+    return host_u16(y)

@@ -173,6 +173,45 @@ def test_quant_and_pack_and_moe_validation_paths():
         assert moe() == DEVICE
 
 
+def test_moe_block_validation_paths():
+    L = mx.lib()
+
+    def cop(**kw):
+        a = dict(elem=1, E=2, Np=96, inter=64, K=128, H=32, ws=A, wsb=256)
+        a.update(kw)
+        return L.mx_moe_copies(a["elem"], a["E"], a["Np"], a["inter"], a["K"], a["H"], A, A, A, A,
+                               A, A, A, A, a["ws"], a["wsb"], None)
+    assert cop(inter=48) == SHAPE            # inter % 32
+    assert cop(inter=128) == SHAPE           # inter > Np
+    assert cop(K=100) == SHAPE
+    assert cop(elem=3) == UNSUP
+    assert cop(ws=None) == NULL
+    assert cop(wsb=100) == WS
+
+    def gu(**kw):
+        a = dict(elem=1, E=8, inter=64, K=256, T=4, topk=2, ldx=256, h=A, ldh=64)
+        a.update(kw)
+        return L.mx_moe_gate_up(a["elem"], a["E"], a["inter"], a["K"], A, A, a["T"], a["topk"],
+                                A, a["ldx"], A, a["h"], a["ldh"], None)
+    assert gu(ldh=32) == SHAPE               # ldh < inter
+    assert gu(ldh=68) == ALIGN
+    assert gu(inter=12) == SHAPE
+    assert gu(h=None) == NULL
+    assert gu(topk=9) == SHAPE
+
+    def dn(**kw):
+        a = dict(elem=1, E=8, H=64, inter=256, T=4, topk=2, ldh=256, wts=None, ws=None, wsb=0)
+        a.update(kw)
+        return L.mx_moe_down(a["elem"], a["E"], a["H"], a["inter"], A, A, a["T"], a["topk"], A,
+                             a["ldh"], A, a["wts"], A, a["ws"], a["wsb"], None)
+    assert dn(ldh=128) == SHAPE              # ldh < inter (K of the down projection)
+    assert dn(wts=A) == WS                   # combined needs the workspace
+    assert dn(H=40) == SHAPE
+    import torch
+    if not torch.cuda.is_available():
+        assert cop() == DEVICE and gu() == DEVICE and dn() == DEVICE
+
+
 def test_binding_raises_without_touching_the_device():
     with pytest.raises(mx.MXError) as ei:
         mx.mx_packed_sizes(0, 0, 1, 24, 512)

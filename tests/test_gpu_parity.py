@@ -444,3 +444,73 @@ def test_moe_edges_long_k(g):
     # no valid id at all: every row zero
     bad = np.full_like(ids, -1)
     assert not g.moe(E2M1, E, N, K, wp, cp, d["x"], bad).any()
+
+
+# ------------------------------------------------------------------ MoE block
+
+def _moe_block_inputs(seed, elem, E, Np, inter, K, H, T, topk):
+    rng = np.random.default_rng(seed)
+    rowb = K // 2 if elem == E2M1 else K
+    gen = (lambda shape: wl.fp4_bytes(rng, shape)) if elem == E2M1 else \
+        (lambda shape: wl.e4m3_bytes(rng, shape))
+    w13 = gen((E, 2 * Np, rowb))
+    w13[:, inter:Np] = 0
+    w13[:, Np + inter:] = 0
+    s13 = wl.codes(rng, (E, 2 * Np, K // 32), 120, 128)
+    w2 = gen((E, H, Np // 2 if elem == E2M1 else Np))
+    w2[:, :, (inter // 2 if elem == E2M1 else inter):] = 0
+    s2 = wl.codes(rng, (E, H, Np // 32), 120, 128)
+    x = wl.activations(rng, (T, K))
+    ids, wts = wl.routing(rng, T, E, topk)
+    return w13, s13, w2, s2, x, ids, wts
+
+
+MOE_BLOCK = [(E2M1, 8, 96, 64, 256, 96, 5, 2), (E2M1, 6, 128, 128, 1024, 64, 16, 4),
+             (E4M3, 4, 64, 32, 160, 48, 3, 2), (E2M1, 4, 576, 576, 512, 64, 4, 2)]
+
+
+@pytest.mark.parametrize("elem,E,Np,inter,K,H,T,topk", MOE_BLOCK)
+def test_moe_block(g, elem, E, Np, inter, K, H, T, topk):
+    """mx_moe_copies bit for bit; mx_moe_gate_up (silu(gate) * up) and
+    mx_moe_down (per-slot hidden rows, per slot and combined) against the
+    oracle; the whole block chained against the oracle's chain with the hidden
+    rows rounded to bf16 in between."""
+    w13, s13, w2, s2, x, ids, wts = _moe_block_inputs([46, elem, E, Np, K], elem, E, Np, inter,
+                                                      K, H, T, topk)
+    ids[0, -1] = -1                               # an id out of range: zero rows
+    o = oracle.moe_copies(elem, E, Np, inter, K, H, w13, s13, w2, s2)
+    gpu = g.moe_copies(elem, E, Np, inter, K, H, w13, s13, w2, s2)
+    for a, b in zip(gpu, o):
+        np.testing.assert_array_equal(a, b)
+    ow13, os13, ow2, os2 = o
+    wp13, cp13 = g.pack(elem, ROW32, E, 2 * inter, K, ow13, os13.reshape(-1))
+    wp2, cp2 = g.pack(elem, ROW32, E, H, inter, ow2, os2.reshape(-1))
+    # up-gate with the fused silu
+    href = oracle.moe_gate_up(elem, E, inter, K, ow13, os13.reshape(-1), x, ids)
+    h = g.moe_gate_up(elem, E, inter, K, wp13, cp13, x, ids, ldh=inter + 8 * (inter % 16 == 0))
+    g.assert_close(h.reshape(T, topk, inter), href, "gate_up")
+    assert not h.reshape(T, topk, inter)[0, -1].any()
+    # down on seeded hidden rows (the same input for both sides)
+    a = wl.activations(np.random.default_rng([47, E, H]), (T * topk, inter))
+    yref = oracle.moe_linear_rows(elem, E, H, inter, ow2, os2.reshape(-1), a, ids)
+    y = g.moe_down(elem, E, H, inter, wp2, cp2, a, ids)
+    g.assert_close(y.reshape(T, topk, H), yref, "down")
+    ycref = oracle.moe_linear_rows(elem, E, H, inter, ow2, os2.reshape(-1), a, ids, wts)
+    yc = g.moe_down(elem, E, H, inter, wp2, cp2, a, ids, wts)
+    g.assert_close(yc.reshape(T, H), ycref, "down combined")
+    # the block: gate_up -> down -> combine, against the oracle's chain (hidden
+    # rows rounded to bf16 between the two products, as the block hands them on)
+    hb = oracle.bf16_round_array(href).reshape(T * topk, inter)
+    chain = oracle.moe_linear_rows(elem, E, H, inter, ow2, os2.reshape(-1), hb, ids, wts)
+    yb = g.moe_down(elem, E, H, inter, wp2, cp2, h, ids, wts)
+    g.assert_close(yb.reshape(T, H), chain, "block")
+
+
+def test_moe_copies_refuses_padding(g):
+    import microscaling_quantized_linear_amd as mx
+    E, Np, inter, K, H = 2, 96, 64, 128, 32
+    w13, s13, w2, s2, _, _, _ = _moe_block_inputs(48, E2M1, E, Np, inter, K, H, 2, 1)
+    w13[1, Np + inter + 1, 3] = 0x22
+    with pytest.raises(mx.MXError) as ei:
+        g.moe_copies(E2M1, E, Np, inter, K, H, w13, s13, w2, s2)
+    assert ei.value.status == 4                   # MX_ERR_VALUE
