@@ -57,7 +57,7 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None,
                     help="run one workload only (gemv16, gemv1, gemv4, gemv16r, a16_c1, a16_c3, "
-                         "moe, gemm)")
+                         "moe, moe_block, gemm)")
     ap.add_argument("--eager", action="store_true",
                     help="launch without HIP graphs (for hardware-counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -275,6 +275,54 @@ def bench_moe(torch, mx, g, wl, steps, warmup):
                 kernel="gemv_kernel (A16W4, MoE)", src="mx_gemv.hip")
 
 
+def bench_moe_block(torch, mx, g, wl, steps, warmup):
+    """MoE block at the MoE decode shape (E = 32 experts, hidden 3072,
+    intermediate 1536, T = 16 tokens, top-8, A16W4): per step the up-gate GEMV
+    over interleaved gate/up rows with the SiLU product fused, then the down
+    projection on the per-slot hidden rows with the weighted combine."""
+    import numpy as np
+    d13 = wl.moe_inputs(4)                                  # w13 rows: [E, 2 inter, K]
+    E, N13, Hd, T, topk = d13["E"], d13["N"], d13["K"], d13["T"], d13["topk"]
+    inter = N13 // 2
+    d2 = wl.moe_inputs(4, N=Hd, K=inter, seed=1)            # w2: [E, hidden, inter]
+    w13p, c13p = g.pack(1, 0, E, N13, Hd, d13["w"], d13["codes"])
+    w2p, c2p = g.pack(1, 0, E, Hd, inter, d2["w"], d2["codes"])
+    per = w13p.numel() + c13p.numel() + w2p.numel() + c2p.numel()
+    nc = max(1, -(-CACHE_BYTES // per))
+    sets = [(w13p, c13p, w2p, c2p)] + [(w13p.clone(), c13p.clone(), w2p.clone(), c2p.clone())
+                                       for _ in range(nc - 1)]
+    x = g.dev(d13["x"])
+    ids = g.dev(d13["ids"])
+    wts = g.dev(d13["weights"])
+    h = torch.empty((T * topk, inter), dtype=torch.int16, device=g.DEV)
+    y = torch.empty((T, Hd), dtype=torch.int16, device=g.DEV)
+    need = mx.mx_moe_workspace(1, E, Hd, inter, T, topk, True)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=g.DEV)
+
+    def gate_up(i):
+        a, b, _, _ = sets[i % nc]
+        mx.mx_moe_gate_up(1, E, inter, Hd, a, b, T, topk, x, Hd, ids, h, inter)
+
+    def step(i):
+        gate_up(i)
+        _, _, a, b = sets[i % nc]
+        mx.mx_moe_down(1, E, Hd, inter, a, b, T, topk, h, inter, ids, wts, y, ws, need)
+
+    timer = GraphTimer(torch)
+    ms_step = timer.time(step, steps, warmup)
+    ms_k = timer.time(gate_up, steps, warmup)
+    touched = len(np.unique(d13["ids"]))
+    b13 = touched * (N13 * Hd // 2 + N13 * (Hd // 32))
+    b2 = touched * (Hd * inter // 2 + Hd * (inter // 32))
+    return dict(workload="mxfp4_a16w4_moe_block_E32_H3072_I1536_T16_top8", E=E, hidden=Hd,
+                inter=inter, T=T, topk=topk, experts_touched=touched, bytes_per_step=b13 + b2,
+                bytes_gate_up=b13, weight_copies=nc, ms_per_step=ms_step, ms_kernel=ms_k,
+                value=(b13 + b2) / (ms_step * 1e-3) / 1e9, unit="GB/s",
+                kernel_gbs=b13 / (ms_k * 1e-3) / 1e9,
+                kernel="gemv_kernel (A16W4, MoE up-gate with SiLU product)",
+                step="mx_moe_gate_up + mx_moe_down (combine)", src="mx_gemv.hip")
+
+
 def bench_gemm(torch, mx, g, wl, steps, warmup):
     """Prefill W8A8 GEMM, M = 4096, N = K = 7168: per step one mx_linear with
     the activation quantized inside the call (T16 layout) then the GEMM; the
@@ -380,6 +428,8 @@ def main():
             sec.append(bench_a16_gemv(torch, mx, g, wl, 3, K, W)); log(json.dumps(sec[-1]))
         if want("moe"):
             sec.append(bench_moe(torch, mx, g, wl, K, W)); log(json.dumps(sec[-1]))
+        if want("moe_block"):
+            sec.append(bench_moe_block(torch, mx, g, wl, K, W)); log(json.dumps(sec[-1]))
         if want("gemm"):
             sec.append(bench_gemm(torch, mx, g, wl, max(10, K // 4), max(3, W // 4)))
             log(json.dumps(sec[-1]))

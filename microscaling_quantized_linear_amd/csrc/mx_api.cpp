@@ -98,13 +98,14 @@ int env_choice(const char *name) {
 // and MX_GEMV_TILES override it (tuning sweeps only; read once).
 // Defaults measured on MI355X with graph-replayed launches: long K (S >= 32
 // steps, e.g. 7168) 8 waves x chunks of 4 steps x 2 tiles; shorter K 4 waves
-// x 4 steps x 1 tile; grouped MoE 4 waves x 2 steps x 4 tiles of an expert.
+// x 4 steps x 1 tile; grouped MoE 2 steps x 4 tiles of an expert, 4 waves from
+// 16 steps (K >= 2048), else 2 (K = 1536 down projection: 17.7 vs 21.0 us).
 mx::GemvShape gemv_shape(int64_t S, bool moe) {
     static const int f_nw = env_choice("MX_GEMV_WAVES"), f_chunk = env_choice("MX_GEMV_CHUNK"),
                      f_tiles = env_choice("MX_GEMV_TILES");
     mx::GemvShape g;
     if (moe)
-        g = {S >= 8 ? 4 : S >= 2 ? 2 : 1, 2, 4};
+        g = {S >= 16 ? 4 : S >= 2 ? 2 : 1, 2, 4};
     else if (S >= 32)
         g = {8, 4, 2};
     else

@@ -325,17 +325,32 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
 }
 
 // Deterministic top-k combine: y[t][n] = sum_k w[t][k] * ys[t*topk + k][n],
-// k ascending, fp32, one bf16 rounding.
+// k ascending, fp32, one bf16 rounding.  A thread owns 4 consecutive outputs
+// (N % 16 == 0) and issues the loads of 8 slots before summing them in order.
 __global__ void __launch_bounds__(256) moe_combine_kernel(int64_t T, int64_t topk, int64_t N,
                                                           const float *__restrict__ ys,
                                                           const float *__restrict__ wts,
                                                           uint16_t *__restrict__ y) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
     if (i >= T * N) return;
     const int64_t t = i / N, n = i % N;
-    float s = 0.f;
-    for (int64_t k = 0; k < topk; ++k) s += wts[t * topk + k] * ys[(t * topk + k) * N + n];
-    y[i] = (uint16_t)bf16_bits(s);
+    v4f s = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t k0 = 0; k0 < topk; k0 += 8) {
+        v4f v[8];
+        float w[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t k = k0 + u < topk ? k0 + u : topk - 1;   // in bounds; unused
+            v[u] = *reinterpret_cast<const v4f *>(ys + (t * topk + k) * N + n);
+            w[u] = wts[t * topk + k];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (k0 + u < topk) s += w[u] * v[u];
+    }
+    const v2u o = {bf16_bits(s[0]) | (bf16_bits(s[1]) << 16),
+                   bf16_bits(s[2]) | (bf16_bits(s[3]) << 16)};
+    *reinterpret_cast<v2u *>(y + i) = o;
 }
 
 template <int ELEM, int LAYOUT, int ACT, bool MOE, int NW, int G>
@@ -391,7 +406,7 @@ hipError_t launch_gemv(int elem, int layout, int act, bool moe, const GemvArgs &
 
 hipError_t launch_moe_combine(int64_t T, int64_t topk, int64_t N, const float *ys,
                               const float *wts, void *y, hipStream_t st) {
-    const int64_t n = T * N;
+    const int64_t n = T * N / 4;
     hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, T,
                        topk, N, ys, wts, (uint16_t *)y);
     return hipGetLastError();
