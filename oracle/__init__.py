@@ -82,6 +82,9 @@ def _declare(L):
     L.orc_moe_gate_up.restype = None
     L.orc_moe_linear_rows.argtypes = [i32, i64, i64, i64, p, p, i64, i64, p, i64, p, p, p]
     L.orc_moe_linear_rows.restype = None
+    L.orc_fold_row_codes.argtypes = [i64, i64, p, p]; L.orc_fold_row_codes.restype = i32
+    L.orc_e4m3_from_dequant.argtypes = [i32, i64, i64, p, i64, p, p]
+    L.orc_e4m3_from_dequant.restype = i64
     L.orc_threads.argtypes = []
     L.orc_threads.restype = i32
 
@@ -274,6 +277,35 @@ def moe_linear_rows(elem, E, N, K, w, codes, a, ids, weights=None):
     lib().orc_moe_linear_rows(elem, E, N, K, _ptr(w), _ptr(codes), T, topk, _ptr(a),
                               a.shape[1], _ptr(ids), _ptr(weights), _ptr(y))
     return y
+
+
+def fold_row_codes(N, KB, codes_row):
+    """[N/32, KB] block codes from row-expanded [N, KB] codes; ValueError when
+    a block's 32 rows disagree (or N is not a multiple of 32)."""
+    c = _c(codes_row, np.uint8)
+    out = np.empty((N // 32, KB), np.uint8)
+    rc = lib().orc_fold_row_codes(N, KB, _ptr(c), _ptr(out))
+    if rc == 1:
+        raise ValueError("row codes are not 32 x 32 blocks")
+    if rc:
+        raise ValueError("bad shape")
+    return out
+
+
+def e4m3_from_dequant(layout, N, K, w_bits, codes, strict=True):
+    """e4m3 bytes [N, K] behind bf16 weights w_bits [N, >= K] (bit patterns)
+    dequantized with `codes` (ROW32 [N, K/32] or BLK32 [N/32, K/32]).  With
+    strict, ValueError when any weight does not come back exactly; else the
+    bytes with 0xFF marking those weights."""
+    w = _c(w_bits, np.uint16)
+    c = _c(codes, np.uint8)
+    out = np.empty((N, K), np.uint8)
+    bad = lib().orc_e4m3_from_dequant(layout, N, K, _ptr(w), w.shape[1], _ptr(c), _ptr(out))
+    if bad < 0:
+        raise ValueError("bad shape")
+    if strict and bad:
+        raise ValueError(f"{bad} of {N * K} values are not e4m3 x scale")
+    return out
 
 
 def threads() -> int:

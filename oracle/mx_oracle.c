@@ -31,6 +31,8 @@
  *       ([weights942] dense_copy); padding never enters a sum.
  *   R5  MoE ids outside [0, E) give all-zero output rows.
  *   R18 the gated activation of the MoE up-gate product is SiLU.
+ *   R20 a bf16-dequantized weight is recovered only when some e4m3 byte times
+ *       its block's scale equals it exactly (a zero keeps its sign).
  *
  * Parity pins: every function here is checked in tests/test_oracle_*.py
  * against closed forms, brute force and exact rational arithmetic.
@@ -516,6 +518,68 @@ int orc_moe_copies(int elem, int64_t E, int64_t Np, int64_t inter, int64_t K,
         }
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Ingest variants: row-expanded codes, bf16-dequantized weights        */
+/* ------------------------------------------------------------------ */
+
+/* [rocm_native] _as_block32_scale, [weights942] linear_copy: a checkpoint's
+ * 32 x 32 block codes that the loader repeated over each block's 32 rows come
+ * back as [N][KB]; folded, out[R][b] = codes_row[32 R][b], provided every one
+ * of rows 32 R .. 32 R + 31 holds that same code in column b.  Returns 1,
+ * writing nothing, when some block's rows disagree (the page raises, or keeps
+ * the row codes); 2 when N is not a positive multiple of 32 or KB < 1. */
+int orc_fold_row_codes(int64_t N, int64_t KB, const uint8_t *codes_row, uint8_t *codes_blk)
+{
+    int64_t R, i, b;
+    if (N < 32 || N % 32 != 0 || KB < 1)
+        return 2;
+    for (R = 0; R < N / 32; R++)
+        for (i = 1; i < 32; i++)
+            for (b = 0; b < KB; b++)
+                if (codes_row[(32 * R + i) * KB + b] != codes_row[32 * R * KB + b])
+                    return 1;
+    for (R = 0; R < N / 32; R++)
+        memcpy(codes_blk + R * KB, codes_row + 32 * R * KB, (size_t)KB);
+    return 0;
+}
+
+/* [weights942] ocp_from_dequant: the e4m3 bytes behind a weight the loader
+ * dequantized to bf16, w[n][k] = dec(byte) * 2^(c - 127), c the code of the
+ * weight's block (layout ROW32: codes [N][K/32]; BLK32: [N/32][K/32]).  The
+ * page's steps: multiply w by 2^(127 - c), round to the nearest e4m3
+ * (orc_e4m3_round: ties to even, sign of zero kept), scale the byte's value
+ * back by 2^(c - 127) and require it to equal w.  Here both scalings are
+ * exact (binary64), so "equal" is equality of the real values (reading R20).
+ * A weight that does not come back -- not e4m3 x 2^(c - 127), NaN, infinite,
+ * or under code 255, which is NaN (reading R6) -- gets the marker 0xFF in out
+ * (a NaN byte, never a valid answer) and is counted.  Returns that count, or
+ * -1 for a shape outside K % 32 == 0 (and N % 32 == 0 for BLK32). */
+int64_t orc_e4m3_from_dequant(int layout, int64_t N, int64_t K, const uint16_t *w,
+                              int64_t ldw, const uint8_t *codes, uint8_t *out)
+{
+    const int64_t KB = K / 32;
+    int64_t n, k, bad = 0;
+    if (N < 1 || K < 32 || K % 32 != 0 || ldw < K ||
+        (layout == ORC_BLK32 && N % 32 != 0))
+        return -1;
+    for (n = 0; n < N; n++)
+        for (k = 0; k < K; k++) {
+            const double v = orc_bf16_value(w[n * ldw + k]);
+            const int c = layout == ORC_BLK32 ? codes[(n / 32) * KB + k / 32]
+                                              : codes[n * KB + k / 32];
+            int byte = 0xFF;
+            if (c != 255 && isfinite(v)) {
+                const int q = orc_e4m3_round(ldexp(v, 127 - c));
+                if (ldexp(orc_e4m3_value(q), c - 127) == v)
+                    byte = q;
+            }
+            if (byte == 0xFF)
+                bad++;
+            out[n * K + k] = (uint8_t)byte;
+        }
+    return bad;
 }
 
 /* SiLU, v * sigmoid(v) = v / (1 + e^-v), in binary64.  The pages pair each
