@@ -22,7 +22,9 @@
  *     (host) are host memory.  The caller allocates and owns every buffer;
  *     the library never allocates device memory in these calls.
  *   - All device work is enqueued on `stream` (0 = the null stream) and the
- *     calls return without synchronizing, except mx_pack_weights (below).
+ *     calls return without synchronizing, except the load-time calls that
+ *     read back a validity flag: mx_pack_weights, mx_fold_row_codes,
+ *     mx_e4m3_from_dequant and mx_moe_copies.
  *   - Arguments are validated on the host before anything is launched; on an
  *     error nothing is launched and outputs are untouched.
  *   - Each call checks that the current device is gfx950 (MX_ERR_DEVICE).
@@ -125,6 +127,41 @@ mx_status mx_pack_weights(int elem, int layout, int64_t E, int64_t N, int64_t K,
                           const void *w, const void *codes, void *w_packed,
                           void *codes_packed, void *ws, size_t ws_bytes,
                           mx_stream_t stream);
+
+/* ---- Ingest of checkpoint forms the packs do not take directly ---- */
+
+/* Fold row-expanded codes back into 32 x 32 block codes ([rocm_native]
+ * _as_block32_scale; [weights942] linear_copy): a loader that repeats each
+ * 32 x 32 block's E8M0 code over the block's 32 rows hands back [N, K/32]
+ * codes; the block codes are then BLK32 codes for mx_pack_weights.
+ *   codes_row (device) [N, ldc] bytes, the first K/32 of each row used
+ *   codes_blk (device) [N/32, K/32] output: codes_blk[R][b] = codes_row[32 R][b]
+ *   ws        (device) at least 256 bytes of scratch, 16-byte aligned
+ * Rules: N % 32 == 0, K % 32 == 0, ldc >= K/32.
+ * Errors: MX_ERR_VALUE when some block's 32 rows do not all hold the same
+ *   code (the output is still written as above but is not the block form;
+ *   keep the row codes, ROW32).  Load-time: synchronizes `stream`. */
+mx_status mx_fold_row_codes(int64_t N, int64_t K, const void *codes_row, int64_t ldc,
+                            void *codes_blk, void *ws, size_t ws_bytes,
+                            mx_stream_t stream);
+
+/* The e4m3 bytes behind a weight the loader dequantized to bf16
+ * ([weights942] ocp_from_dequant): w[n][k] = dec(byte) * 2^(c - 127), c the
+ * code of the weight's block.
+ *   layout  MX_SCALE_ROW32 (codes [N, K/32]) or MX_SCALE_BLK32 ([N/32, K/32])
+ *   w_bf16  (device) [N, ldw] bf16, 16-byte aligned, ldw % 8 == 0
+ *   codes   (device) the codes the weight was dequantized with
+ *   w_out   (device) [N, K] e4m3 bytes, 16-byte aligned
+ *   ws      (device) at least 256 bytes of scratch, 16-byte aligned
+ * A weight is recovered only when some finite e4m3 byte times 2^(c - 127)
+ * equals it exactly; a zero keeps its sign (-0 -> 0x80).
+ * Errors: MX_ERR_VALUE when some weight is not recovered -- not of that
+ *   form, NaN, infinite, or under code 255 (NaN).  Its output byte is then
+ *   0xFF (an e4m3 NaN, never a recovered value); every other byte is still
+ *   recovered.  Load-time: synchronizes `stream`. */
+mx_status mx_e4m3_from_dequant(int layout, int64_t N, int64_t K, const void *w_bf16,
+                               int64_t ldw, const void *codes, void *w_out, void *ws,
+                               size_t ws_bytes, mx_stream_t stream);
 
 /* Per-token MXFP8 activation quantization ([rocm_native] _quant_mxfp8_tile;
  * rule as in mx_quant_rule).

@@ -23,7 +23,7 @@ __all__ = [
     "mx_packed_sizes", "mx_pack_weights", "mx_quant_act", "mx_act_t16_sizes",
     "mx_quant_act_t16", "mx_linear_workspace",
     "mx_linear", "mx_moe_workspace", "mx_moe_linear", "mx_moe_copies", "mx_moe_gate_up",
-    "mx_moe_down", "mx_status_str",
+    "mx_moe_down", "mx_fold_row_codes", "mx_e4m3_from_dequant", "mx_status_str",
     "mx_arch_supported",
 ]
 
@@ -72,9 +72,12 @@ def lib() -> C.CDLL:
         L.mx_moe_gate_up.argtypes = [i32, i64, i64, i64, p, p, i64, i64, p, i64, p, p, i64, p]
         L.mx_moe_down.argtypes = [i32, i64, i64, i64, p, p, i64, i64, p, i64, p, p, p, p, sz,
                                   p]
+        L.mx_fold_row_codes.argtypes = [i64, i64, p, i64, p, p, sz, p]
+        L.mx_e4m3_from_dequant.argtypes = [i32, i64, i64, p, i64, p, p, p, sz, p]
         for name in ("mx_packed_sizes", "mx_pack_weights", "mx_quant_act", "mx_act_t16_sizes",
                      "mx_quant_act_t16", "mx_linear_workspace", "mx_linear", "mx_moe_workspace",
-                     "mx_moe_linear", "mx_moe_copies", "mx_moe_gate_up", "mx_moe_down"):
+                     "mx_moe_linear", "mx_moe_copies", "mx_moe_gate_up", "mx_moe_down",
+                     "mx_fold_row_codes", "mx_e4m3_from_dequant"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -188,3 +191,14 @@ def mx_moe_down(elem, E, H, inter, w2_packed, codes_packed, T, topk, h, ldh, top
     _check(lib().mx_moe_down(elem, E, H, inter, _ptr(w2_packed), _ptr(codes_packed), T, topk,
                              _ptr(h), ldh, _ptr(topk_ids), _ptr(topk_weights), _ptr(y),
                              _ptr(ws), ws_bytes, _stream(stream)), "mx_moe_down")
+
+
+def mx_fold_row_codes(N, K, codes_row, ldc, codes_blk, ws, ws_bytes, stream=None):
+    _check(lib().mx_fold_row_codes(N, K, _ptr(codes_row), ldc, _ptr(codes_blk), _ptr(ws),
+                                   ws_bytes, _stream(stream)), "mx_fold_row_codes")
+
+
+def mx_e4m3_from_dequant(layout, N, K, w_bf16, ldw, codes, w_out, ws, ws_bytes, stream=None):
+    _check(lib().mx_e4m3_from_dequant(layout, N, K, _ptr(w_bf16), ldw, _ptr(codes), _ptr(w_out),
+                                      _ptr(ws), ws_bytes, _stream(stream)),
+           "mx_e4m3_from_dequant")

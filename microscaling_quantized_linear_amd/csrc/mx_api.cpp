@@ -165,6 +165,20 @@ mx_status moe_run(int elem, int64_t E, int64_t N, int64_t K, const void *w_packe
     return MX_OK;
 }
 
+// Load-time checks end with a device flag read back: clear it, run the check,
+// copy it to the host and wait for the stream.
+template <class F>
+mx_status flagged(void *ws, hipStream_t s, F launch) {
+    int *bad = static_cast<int *>(ws);
+    if (hipMemsetAsync(bad, 0, sizeof(int), s) != hipSuccess) return MX_ERR_LAUNCH;
+    mx_status st = launched(launch(bad));
+    if (st != MX_OK) return st;
+    int h = 0;
+    if (hipMemcpyAsync(&h, bad, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return MX_ERR_LAUNCH;
+    return h ? MX_ERR_VALUE : MX_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -464,18 +478,45 @@ mx_status mx_moe_copies(int elem, int64_t E, int64_t Np, int64_t inter, int64_t 
     mx_status st = device_ok();
     if (st != MX_OK) return st;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    int *bad = static_cast<int *>(ws);
-    if (hipMemsetAsync(bad, 0, sizeof(int), s) != hipSuccess) return MX_ERR_LAUNCH;
-    if ((st = launched(mx::launch_moe_padding_check(elem, E, Np, inter, K, H, w13, w2, bad, s))) !=
-        MX_OK)
+    if ((st = flagged(ws, s, [&](int *bad) {
+             return mx::launch_moe_padding_check(elem, E, Np, inter, K, H, w13, w2, bad, s);
+         })) != MX_OK)
         return st;
-    int h = 0;
-    if (hipMemcpyAsync(&h, bad, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess ||
-        hipStreamSynchronize(s) != hipSuccess)
-        return MX_ERR_LAUNCH;
-    if (h) return MX_ERR_VALUE;
     return launched(mx::launch_moe_copies(elem, E, Np, inter, K, H, w13, s13, w2, s2, w13_out,
                                           s13_out, w2_out, s2_out, s));
+}
+
+mx_status mx_fold_row_codes(int64_t N, int64_t K, const void *codes_row, int64_t ldc,
+                            void *codes_blk, void *ws, size_t ws_bytes, mx_stream_t stream) {
+    if (N < 32 || N % 32 != 0 || K < 32 || K % 32 != 0 || ldc < K / 32) return MX_ERR_SHAPE;
+    if (N * ldc > kMaxRsrc) return MX_ERR_SHAPE;
+    if (!codes_row || !codes_blk || !ws) return MX_ERR_NULL;
+    if (!aligned16(ws)) return MX_ERR_ALIGN;
+    if (ws_bytes < 256) return MX_ERR_WORKSPACE;
+    mx_status st = device_ok();
+    if (st != MX_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return flagged(ws, s, [&](int *bad) {
+        return mx::launch_fold_codes(N, K / 32, ldc, codes_row, codes_blk, bad, s);
+    });
+}
+
+mx_status mx_e4m3_from_dequant(int layout, int64_t N, int64_t K, const void *w_bf16,
+                               int64_t ldw, const void *codes, void *w_out, void *ws,
+                               size_t ws_bytes, mx_stream_t stream) {
+    if (layout != ROW32 && layout != BLK32) return MX_ERR_UNSUPPORTED;
+    if (N < 1 || K < 32 || K % 32 != 0 || ldw < K || (layout == BLK32 && N % 32 != 0))
+        return MX_ERR_SHAPE;
+    if (!w_bf16 || !codes || !w_out || !ws) return MX_ERR_NULL;
+    if (!aligned16(w_bf16) || ldw % 8 != 0 || !aligned16(w_out) || !aligned16(ws))
+        return MX_ERR_ALIGN;
+    if (ws_bytes < 256) return MX_ERR_WORKSPACE;
+    mx_status st = device_ok();
+    if (st != MX_OK) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    return flagged(ws, s, [&](int *bad) {
+        return mx::launch_e4m3_from_bf16(layout, N, K, w_bf16, ldw, codes, w_out, bad, s);
+    });
 }
 
 mx_status mx_moe_gate_up(int elem, int64_t E, int64_t inter, int64_t K, const void *w13_packed,

@@ -66,6 +66,10 @@ hipError_t launch_moe_copies(int elem, int64_t E, int64_t Np, int64_t inter, int
                              int64_t H, const void *w13, const void *s13, const void *w2,
                              const void *s2, void *ow13, void *os13, void *ow2, void *os2,
                              hipStream_t stream);
+hipError_t launch_fold_codes(int64_t N, int64_t KB, int64_t ldc, const void *in, void *out,
+                             int *bad, hipStream_t st);
+hipError_t launch_e4m3_from_bf16(int layout, int64_t N, int64_t K, const void *w, int64_t ldw,
+                                 const void *codes, void *out, int *bad, hipStream_t st);
 hipError_t launch_quant(int64_t M, int64_t K, const void *x, int64_t ldx, void *xq, int64_t ldq,
                         void *xcodes, int64_t ldc, int rule, hipStream_t stream);
 // Launch shape of the GEMV: nw wavefronts per workgroup (1, 2, 4, 8) split

@@ -212,6 +212,36 @@ def test_moe_block_validation_paths():
         assert cop() == DEVICE and gu() == DEVICE and dn() == DEVICE
 
 
+def test_ingest_validation_paths():
+    L = mx.lib()
+
+    def fold(**kw):
+        a = dict(N=64, K=128, ldc=4, out=A, ws=A, wsb=256)
+        a.update(kw)
+        return L.mx_fold_row_codes(a["N"], a["K"], A, a["ldc"], a["out"], a["ws"], a["wsb"], None)
+    assert fold(N=48) == SHAPE               # N % 32
+    assert fold(K=100) == SHAPE
+    assert fold(ldc=3) == SHAPE              # ldc < K / 32
+    assert fold(out=None) == NULL
+    assert fold(wsb=16) == WS
+
+    def rec(**kw):
+        a = dict(layout=1, N=64, K=128, ldw=128, out=A, ws=A, wsb=256)
+        a.update(kw)
+        return L.mx_e4m3_from_dequant(a["layout"], a["N"], a["K"], A, a["ldw"], A, a["out"],
+                                      a["ws"], a["wsb"], None)
+    assert rec(layout=2) == UNSUP
+    assert rec(N=48) == SHAPE                # BLK32 needs N % 32
+    assert rec(K=96 + 8) == SHAPE
+    assert rec(ldw=120) == SHAPE             # ldw < K
+    assert rec(ldw=132) == ALIGN             # ldw % 8
+    assert rec(out=None) == NULL
+    assert rec(wsb=0) == WS
+    import torch
+    if not torch.cuda.is_available():
+        assert fold() == DEVICE and rec() == DEVICE and rec(layout=0, N=48) == DEVICE
+
+
 def test_binding_raises_without_touching_the_device():
     with pytest.raises(mx.MXError) as ei:
         mx.mx_packed_sizes(0, 0, 1, 24, 512)

@@ -1,0 +1,172 @@
+"""Parity of the ingest entry points (mx_fold_row_codes, mx_e4m3_from_dequant)
+with the oracle, through the C ABI: bytes and status bit for bit, including
+the 0xFF markers of weights that are not recovered; then the whole ingest
+chain (fold, pack, linear) at the 7168 x 7168 decode shape."""
+import numpy as np
+import pytest
+
+import oracle
+from microscaling_quantized_linear_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+E4M3, ROW32, BLK32, BF16 = 0, 0, 1, 0
+MX_ERR_VALUE = 4
+
+
+@pytest.fixture(scope="module")
+def g():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mxgpu
+    return mxgpu
+
+
+def _status(fn):
+    import microscaling_quantized_linear_amd as mx
+    try:
+        fn()
+        return 0
+    except mx.MXError as e:
+        return e.status
+
+
+def _fold(g, N, K, rows):
+    import torch
+    import microscaling_quantized_linear_amd as mx
+    c = g.dev(rows)
+    out = torch.full((N // 32, K // 32), 0xAB, dtype=torch.uint8, device=g.DEV)
+    ws = torch.empty(256, dtype=torch.uint8, device=g.DEV)
+    st = _status(lambda: mx.mx_fold_row_codes(N, K, c, rows.shape[1], out, ws, 256))
+    torch.cuda.synchronize()
+    return st, out.cpu().numpy()
+
+
+def _recover(g, layout, N, K, w_bits, codes):
+    import torch
+    import microscaling_quantized_linear_amd as mx
+    w = g.dev(w_bits)
+    c = g.dev(codes)
+    out = torch.full((N, K), 0xAB, dtype=torch.uint8, device=g.DEV)
+    ws = torch.empty(256, dtype=torch.uint8, device=g.DEV)
+    st = _status(lambda: mx.mx_e4m3_from_dequant(layout, N, K, w, w_bits.shape[1], c, out, ws,
+                                                 256))
+    torch.cuda.synchronize()
+    return st, out.cpu().numpy()
+
+
+def _dequant_bf16(q, rows):
+    """bf16 bit patterns of dec(q) * 2^(code - 127) (rows: row-expanded
+    codes), through torch's CPU cast of the exact binary64 product."""
+    import torch
+    b = np.array([i for i in range(256) if i & 0x7F != 0x7F], np.uint8)
+    val = np.zeros(256)
+    val[b] = torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    scale = np.ldexp(1.0, rows.astype(np.int64) - 127).repeat(32, axis=1)
+    v = val[q] * scale
+    return torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+# ------------------------------------------------------------------ fold
+
+@pytest.mark.parametrize("N,K,ldc", [(32, 32, 1), (96, 224, 9), (256, 1568, 49),
+                                     (7168, 7168, 224)])
+def test_fold_matches_oracle(g, N, K, ldc):
+    rng = np.random.default_rng([91, N, K])
+    KB = K // 32
+    blk = wl.codes(rng, (N // 32, KB), 118, 132)
+    rows = np.zeros((N, ldc), np.uint8)
+    rows[:, :KB] = np.repeat(blk, 32, axis=0)
+    rows[:, KB:] = 0x5A                                 # beyond K/32: not read
+    st, got = _fold(g, N, K, rows)
+    assert st == 0
+    np.testing.assert_array_equal(got, oracle.fold_row_codes(N, KB, rows[:, :KB]))
+    # one row of one block disagrees: refused, output still row 32 R's codes
+    bad = rows.copy()
+    r = int(rng.integers(N))
+    bad[r, int(rng.integers(KB))] ^= 0x10
+    st, got = _fold(g, N, K, bad)
+    assert st == MX_ERR_VALUE
+    with pytest.raises(ValueError):
+        oracle.fold_row_codes(N, KB, bad[:, :KB])
+    np.testing.assert_array_equal(got, bad[::32, :KB])
+
+
+# ------------------------------------------------------------------ e4m3 from bf16
+
+@pytest.mark.parametrize("code", [0, 1, 3, 4, 9, 100, 127, 150, 246, 250, 254, 255])
+def test_recover_all_bf16_patterns(g, code):
+    """Every bf16 pattern under one block code: GPU bytes (0xFF where not
+    recovered) and status equal the oracle's."""
+    N, K = 2048, 32
+    w = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(N, K)
+    codes = np.full((N // 32, 1), code, np.uint8)
+    want = oracle.e4m3_from_dequant(BLK32, N, K, w, codes, strict=False)
+    st, got = _recover(g, BLK32, N, K, w, codes)
+    np.testing.assert_array_equal(got, want)
+    assert st == (MX_ERR_VALUE if (want == 0xFF).any() else 0)
+    # row-expanded codes give the same bytes
+    st2, got2 = _recover(g, ROW32, N, K, w, np.full((N, 1), code, np.uint8))
+    np.testing.assert_array_equal(got2, want)
+    assert st2 == st
+
+
+@pytest.mark.parametrize("layout,N,K,ldw", [(BLK32, 64, 96, 96), (ROW32, 48, 160, 168),
+                                            (BLK32, 256, 1568, 1576)])
+def test_recover_round_trip_and_one_bad_weight(g, layout, N, K, ldw):
+    rng = np.random.default_rng([92, layout, N, K])
+    q = wl.e4m3_bytes(rng, (N, K))
+    q[0, :4] = [0x00, 0x80, 0x01, 0x81]
+    if layout == BLK32:
+        codes = wl.codes(rng, (N // 32, K // 32), 100, 150)
+        rows = np.repeat(codes, 32, axis=0)
+    else:
+        codes = rows = wl.codes(rng, (N, K // 32), 100, 150)
+    w = np.zeros((N, ldw), np.uint16)
+    w[:, :K] = _dequant_bf16(q, rows)
+    st, got = _recover(g, layout, N, K, w, codes)
+    assert st == 0
+    np.testing.assert_array_equal(got, q)
+    np.testing.assert_array_equal(got, oracle.e4m3_from_dequant(layout, N, K, w, codes))
+    i = tuple(np.argwhere((w[:, :K] & 0x7F80) != 0)[int(rng.integers(100))])
+    w[i] ^= 1
+    st, got = _recover(g, layout, N, K, w, codes)
+    assert st == MX_ERR_VALUE
+    np.testing.assert_array_equal(got, oracle.e4m3_from_dequant(layout, N, K, w, codes,
+                                                                strict=False))
+    assert got[i] == 0xFF
+
+
+def test_ingest_chain_at_decode_shape(g):
+    """The 7168 x 7168 decode weight as a loader hands it over -- dequantized
+    to bf16 with row-expanded codes -- recovered, folded and packed BLK32,
+    gives the same bytes and codes as the checkpoint, and the same GEMV
+    output (bit for bit) as the checkpoint packed directly."""
+    import torch
+    import microscaling_quantized_linear_amd as mx
+    d = wl.linear_inputs(2, M=16)
+    N, K = d["N"], d["K"]
+    blk = d["codes"].reshape(N // 32, K // 32)
+    rows = np.repeat(blk, 32, axis=0)
+    w = _dequant_bf16(d["w"], rows)
+    st, folded = _fold(g, N, K, rows)
+    assert st == 0
+    np.testing.assert_array_equal(folded, blk)
+    st, q = _recover(g, BLK32, N, K, w, folded)
+    assert st == 0
+    np.testing.assert_array_equal(q, d["w"])
+    x = g.dev(d["x"])
+    ys = []
+    for wb, cb in ((q, folded), (d["w"], blk)):
+        wp, cp = g.pack(E4M3, BLK32, 1, N, K, wb, cb)
+        y = torch.empty((16, N), dtype=torch.int16, device=g.DEV)
+        mx.mx_linear(E4M3, BLK32, N, K, wp, cp, 16, BF16, 0, x, K, None, 0, None, 0, None, y,
+                     N, None, 0)
+        torch.cuda.synchronize()
+        ys.append(g.host_u16(y))
+    np.testing.assert_array_equal(ys[0], ys[1])
+    ref = oracle.linear_pairs(E4M3, BLK32, N, K, d["w"], d["codes"], BF16,
+                              np.arange(16).repeat(8), np.arange(0, N, 56)[:128], x=d["x"])
+    g.assert_close(ys[0][np.arange(16).repeat(8), np.arange(0, N, 56)[:128]], ref,
+                   "ingest chain")
