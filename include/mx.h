@@ -317,6 +317,20 @@ mx_status mx_moe_down(int elem, int64_t E, int64_t H, int64_t inter,
                       const int32_t *topk_ids, const float *topk_weights,
                       void *y, void *ws, size_t ws_bytes, mx_stream_t stream);
 
+/* Batch-invariant mode ([rocm_native] process_weights_after_loading: under
+ * VLLM_BATCH_INVARIANT the page leaves its block-scaled GEMM, whose split of
+ * K varies with M).  Here the decode GEMVs (every A16 call, W8A8 with
+ * M <= 64, and the MoE) sum each output in an order fixed by K alone, so a
+ * row's result does not depend on the number of rows in the call; W8A8 with
+ * M > 64 runs the prefill GEMM, which sums in another order.  With the mode
+ * on, W8A8 runs the GEMV for every M: every row's output is then bit-identical
+ * to the same row computed in any other call, at the cost of re-reading the
+ * weights once per 16 rows.  Process-wide and read at each call; set it before
+ * sizing workspaces (mx_linear_workspace depends on it).  The environment
+ * variable MX_BATCH_INVARIANT=1 turns it on at start-up.  Returns the previous
+ * setting (0 or 1). */
+int mx_set_batch_invariant(int on);
+
 /* Static description of a status code (never NULL). */
 const char *mx_status_str(mx_status status);
 

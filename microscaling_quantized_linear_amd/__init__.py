@@ -23,7 +23,7 @@ __all__ = [
     "mx_packed_sizes", "mx_pack_weights", "mx_quant_act", "mx_act_t16_sizes",
     "mx_quant_act_t16", "mx_linear_workspace",
     "mx_linear", "mx_moe_workspace", "mx_moe_linear", "mx_moe_copies", "mx_moe_gate_up",
-    "mx_moe_down", "mx_fold_row_codes", "mx_e4m3_from_dequant", "mx_status_str",
+    "mx_moe_down", "mx_fold_row_codes", "mx_e4m3_from_dequant", "mx_set_batch_invariant", "mx_status_str",
     "mx_arch_supported",
 ]
 
@@ -72,6 +72,8 @@ def lib() -> C.CDLL:
         L.mx_moe_gate_up.argtypes = [i32, i64, i64, i64, p, p, i64, i64, p, i64, p, p, i64, p]
         L.mx_moe_down.argtypes = [i32, i64, i64, i64, p, p, i64, i64, p, i64, p, p, p, p, sz,
                                   p]
+        L.mx_set_batch_invariant.argtypes = [i32]
+        L.mx_set_batch_invariant.restype = i32
         L.mx_fold_row_codes.argtypes = [i64, i64, p, i64, p, p, sz, p]
         L.mx_e4m3_from_dequant.argtypes = [i32, i64, i64, p, i64, p, p, p, sz, p]
         for name in ("mx_packed_sizes", "mx_pack_weights", "mx_quant_act", "mx_act_t16_sizes",
@@ -202,3 +204,8 @@ def mx_e4m3_from_dequant(layout, N, K, w_bf16, ldw, codes, w_out, ws, ws_bytes, 
     _check(lib().mx_e4m3_from_dequant(layout, N, K, _ptr(w_bf16), ldw, _ptr(codes), _ptr(w_out),
                                       _ptr(ws), ws_bytes, _stream(stream)),
            "mx_e4m3_from_dequant")
+
+
+def mx_set_batch_invariant(on: bool) -> bool:
+    """Turn the process-wide batch-invariant mode on or off; the previous setting."""
+    return bool(lib().mx_set_batch_invariant(1 if on else 0))

@@ -27,6 +27,27 @@ constexpr int64_t kMaxRsrc = (int64_t(1) << 31) - 1;   // 32-bit buffer offsets
 // largest M served by the decode GEMV for W8A8; above it the GEMM runs
 constexpr int64_t kGemvMaxM = 64;
 
+// Batch-invariant mode: every W8A8 M runs on the decode GEMV, whose order of
+// summation for an output depends on K alone, so a row's result does not
+// depend on how many rows share the call (the GEMM above kGemvMaxM sums in
+// another order).  Process-wide; MX_BATCH_INVARIANT=1 sets it at start-up and
+// mx_set_batch_invariant changes it.
+std::atomic<int> g_invariant{-1};
+bool batch_invariant() {
+    int v = g_invariant.load(std::memory_order_relaxed);
+    if (v < 0) {
+        const char *s = std::getenv("MX_BATCH_INVARIANT");
+        int unset = -1;
+        g_invariant.compare_exchange_strong(unset, s && s[0] && s[0] != '0' ? 1 : 0);
+        v = g_invariant.load(std::memory_order_relaxed);
+    }
+    return v == 1;
+}
+// the W8A8 prefill GEMM serves this call (else a GEMV)
+bool use_gemm(int act, int64_t M) {
+    return act != ACT_BF16 && M > kGemvMaxM && !batch_invariant();
+}
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
 
@@ -198,6 +219,12 @@ const char *mx_status_str(mx_status s) {
     return "unknown status";
 }
 
+int mx_set_batch_invariant(int on) {
+    const int prev = batch_invariant() ? 1 : 0;
+    g_invariant.store(on ? 1 : 0, std::memory_order_relaxed);
+    return prev;
+}
+
 int mx_arch_supported(const char *name) {
     if (!name) return 0;
     return std::strncmp(name, "gfx950", 6) == 0 && (name[6] == '\0' || name[6] == ':');
@@ -281,14 +308,15 @@ mx_status mx_linear_workspace(int elem, int layout, int64_t N, int64_t K, int64_
     if (M < 1) return MX_ERR_SHAPE;
     if (act != ACT_BF16 && act != ACT_MXFP8 && act != ACT_MXFP8_T16) return MX_ERR_UNSUPPORTED;
     *bytes = 0;
-    const bool long_k = M <= kGemvMaxM && !gemv_w8_plan(N, K, M).ok;
+    const bool gemm = use_gemm(act, M);
+    const bool long_k = !gemm && !gemv_w8_plan(N, K, M).ok;
     if (act == ACT_MXFP8 && !prequantized && fused_quant_ok(elem, N, K, M))
         return MX_OK;                                   // quantized inside the GEMV
     if (act == ACT_MXFP8 && !prequantized && !long_k)   // in-call quantization into T16
         *bytes = (size_t)(round256(mx::act_t16_data_bytes(M, K)) + mx::act_codes_t16_bytes(M, K));
     else if (act == ACT_MXFP8 && !prequantized)         // row-major, chunked GEMV for long K
         *bytes = (size_t)(round256(M * padded_k(K)) + round256(M * (padded_k(K) / 32)));
-    else if (act == ACT_MXFP8 && M > kGemvMaxM)         // row-major input restaged into T16
+    else if (act == ACT_MXFP8 && gemm)                  // row-major input restaged into T16
         *bytes = (size_t)(round256(mx::act_t16_data_bytes(M, K)) + mx::act_codes_t16_bytes(M, K));
     return MX_OK;
 }
@@ -332,7 +360,7 @@ mx_status mx_linear(int elem, int layout, int64_t N, int64_t K, const void *w_pa
     mx_linear_workspace(elem, layout, N, K, M, act, incall ? 0 : 1, &need);
     if (need > 0 && (!ws || ws_bytes < need)) return MX_ERR_WORKSPACE;
     if (need > 0 && !aligned16(ws)) return MX_ERR_ALIGN;
-    const bool gemm = act != ACT_BF16 && M > kGemvMaxM;
+    const bool gemm = use_gemm(act, M);
     if (gemm && N * Kp > kMaxRsrc) return MX_ERR_SHAPE;
     if ((st = device_ok()) != MX_OK) return st;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);

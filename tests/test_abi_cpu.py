@@ -242,6 +242,23 @@ def test_ingest_validation_paths():
         assert fold() == DEVICE and rec() == DEVICE and rec(layout=0, N=48) == DEVICE
 
 
+def test_batch_invariant_switch_and_workspace():
+    """The mode switch returns the previous setting; with it on, a
+    row-major pre-quantized W8A8 call above 64 rows needs no restaging
+    workspace (it runs the GEMV, not the GEMM)."""
+    prev = mx.mx_set_batch_invariant(False)
+    try:
+        assert mx.mx_linear_workspace(0, 1, 512, 1024, 200, 1, True) > 0
+        assert mx.mx_linear_workspace(0, 1, 512, 1024, 64, 1, True) == 0
+        assert mx.mx_set_batch_invariant(True) is False
+        assert mx.mx_linear_workspace(0, 1, 512, 1024, 200, 1, True) == 0
+        # in-call quantization: the T16 staging either way
+        assert mx.mx_linear_workspace(0, 1, 512, 1024, 200, 1, False) > 0
+        assert mx.mx_set_batch_invariant(True) is True
+    finally:
+        mx.mx_set_batch_invariant(prev)
+
+
 def test_binding_raises_without_touching_the_device():
     with pytest.raises(mx.MXError) as ei:
         mx.mx_packed_sizes(0, 0, 1, 24, 512)
