@@ -83,3 +83,29 @@ def test_graph_moe_combined(env):
         mx.mx_moe_linear(1, E, N, K, wp, cp, T, topk, x, K, ids, wts, y, ws, need)
 
     _replays_match(torch, run, y, lambda: ws[16384:].fill_(3))
+
+
+def test_graph_moe_block(env):
+    """Up-gate with the SiLU product, then the combined down projection,
+    captured as one graph."""
+    torch, mx, g = env
+    E, inter, H, T, topk = 8, 64, 96, 5, 2
+    d13 = wl.moe_inputs(4, E=E, N=2 * inter, K=H, T=T, topk=topk)
+    d2 = wl.moe_inputs(4, E=E, N=H, K=inter, T=T, topk=topk, seed=1)
+    w13p, c13p = g.pack(1, 0, E, 2 * inter, H, d13["w"], d13["codes"])
+    w2p, c2p = g.pack(1, 0, E, H, inter, d2["w"], d2["codes"])
+    x, ids, wts = g.dev(d13["x"]), g.dev(d13["ids"]), g.dev(d13["weights"])
+    h = torch.empty((T * topk, inter), dtype=torch.int16, device=g.DEV)
+    y = torch.empty((T, H), dtype=torch.int16, device=g.DEV)
+    need = mx.mx_moe_workspace(1, E, H, inter, T, topk, 1)
+    ws = torch.zeros(need, dtype=torch.uint8, device=g.DEV)
+
+    def run():
+        mx.mx_moe_gate_up(1, E, inter, H, w13p, c13p, T, topk, x, H, ids, h, inter)
+        mx.mx_moe_down(1, E, H, inter, w2p, c2p, T, topk, h, inter, ids, wts, y, ws, need)
+
+    def other():
+        h.fill_(5)
+        ws.fill_(9)
+
+    _replays_match(torch, run, y, other)
