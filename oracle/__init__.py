@@ -85,6 +85,10 @@ def _declare(L):
     L.orc_fold_row_codes.argtypes = [i64, i64, p, p]; L.orc_fold_row_codes.restype = i32
     L.orc_e4m3_from_dequant.argtypes = [i32, i64, i64, p, i64, p, p]
     L.orc_e4m3_from_dequant.restype = i64
+    L.orc_q_fused_perm.argtypes = [i64, i64, p]; L.orc_q_fused_perm.restype = i32
+    L.orc_o_fused_perm.argtypes = [i64, i64, p]; L.orc_o_fused_perm.restype = i32
+    L.orc_fused_layout_permute.argtypes = [i32, i32, i64, i64, i64, p, p, p, p]
+    L.orc_fused_layout_permute.restype = i32
     L.orc_threads.argtypes = []
     L.orc_threads.restype = i32
 
@@ -306,6 +310,36 @@ def e4m3_from_dequant(layout, N, K, w_bits, codes, strict=True):
     if strict and bad:
         raise ValueError(f"{bad} of {N * K} values are not e4m3 x scale")
     return out
+
+
+def q_fused_perm(H, D):
+    """perm with fused = standard[perm] for the attention kernel's Q layout."""
+    perm = np.empty(H * D, np.int64)
+    if lib().orc_q_fused_perm(H, D, _ptr(perm)):
+        raise ValueError("D must be a multiple of 16")
+    return perm
+
+
+def o_fused_perm(G, D):
+    """perm with fused = standard[perm] for the attention kernel's O layout."""
+    perm = np.empty(G * D, np.int64)
+    if lib().orc_o_fused_perm(G, D, _ptr(perm)):
+        raise ValueError("D must be a multiple of 32")
+    return perm
+
+
+def fused_layout_permute(kind, layout, N, K, heads, w, codes):
+    """Q rows (kind 0) or O columns (kind 1) of an MXFP8 weight [N, K] and
+    its codes, in the attention kernel's layout."""
+    w = _c(w, np.uint8)
+    codes = _c(codes, np.uint8)
+    wo = np.empty((N, K), np.uint8)
+    co = np.empty_like(codes)
+    rc = lib().orc_fused_layout_permute(kind, layout, N, K, heads, _ptr(w), _ptr(codes),
+                                        _ptr(wo), _ptr(co))
+    if rc:
+        raise ValueError("shape or layout outside the permutation")
+    return wo, co
 
 
 def threads() -> int:

@@ -582,6 +582,93 @@ int64_t orc_e4m3_from_dequant(int layout, int64_t N, int64_t K, const uint16_t *
     return bad;
 }
 
+/* ------------------------------------------------------------------ */
+/* Load-time layout permutations for the attention-adjacent linears     */
+/* ------------------------------------------------------------------ */
+
+/* [fused_layout] q_fused_permutation: the attention kernel reads Q with each
+ * head's D values cut into 16-value chunks, chunk d/16 of every head side by
+ * side: fused index (d / 16) H 16 + h 16 + d % 16 holds standard index
+ * h D + d.  perm[f] = the standard index at fused index f (fused =
+ * standard[perm]).  Returns 1 when D % 16 != 0. */
+int orc_q_fused_perm(int64_t H, int64_t D, int64_t *perm)
+{
+    int64_t h, d;
+    if (H < 1 || D < 16 || D % 16 != 0)
+        return 1;
+    for (h = 0; h < H; h++)
+        for (d = 0; d < D; d++)
+            perm[(d / 16) * H * 16 + h * 16 + d % 16] = h * D + d;
+    return 0;
+}
+
+/* [fused_layout] o_fused_permutation: the kernel writes O for the G heads of
+ * a group with each head's D values cut into 32-value chunks, chunk c of
+ * every head side by side: fused index (c G + h) 32 + j holds standard index
+ * h D + c 32 + j.  Returns 1 when D % 32 != 0. */
+int orc_o_fused_perm(int64_t G, int64_t D, int64_t *perm)
+{
+    int64_t h, c, j;
+    if (G < 1 || D < 32 || D % 32 != 0)
+        return 1;
+    for (h = 0; h < G; h++)
+        for (c = 0; c < D / 32; c++)
+            for (j = 0; j < 32; j++)
+                perm[(c * G + h) * 32 + j] = h * D + c * 32 + j;
+    return 0;
+}
+
+/* [fused_layout] permute_wq_b_: the rows of an MXFP8 weight [N, K] and of
+ * its per-row codes [N, K/32] gathered by the Q permutation of `heads` heads
+ * of D = N / heads rows: out row f = in row perm[f].  permute_wo_a_: the
+ * input columns of [N, K] gathered by the O permutation of `heads` heads of
+ * D = K / heads columns, and the code columns (one per 32 columns, layout
+ * ROW32 [N, K/32] or BLK32 [N/32, K/32]) by its per-chunk form, perm[32 f] /
+ * 32.  kind 0 = Q rows (ROW32 codes only: a 32-row block would straddle two
+ * heads), 1 = O columns.  Returns 1 for shapes the permutation does not
+ * divide, 2 for Q rows with BLK32 codes. */
+int orc_fused_layout_permute(int kind, int layout, int64_t N, int64_t K, int64_t heads,
+                             const uint8_t *w, const uint8_t *codes, uint8_t *w_out,
+                             uint8_t *codes_out)
+{
+    const int64_t KB = K / 32;
+    int64_t *perm, f, n;
+    if (heads < 1 || K < 32 || K % 32 != 0 || N < 1)
+        return 1;
+    if (kind == 0) {
+        if (layout != ORC_ROW32)
+            return 2;
+        if (N % heads != 0)
+            return 1;
+        perm = malloc((size_t)N * sizeof *perm);
+        if (orc_q_fused_perm(heads, N / heads, perm)) {
+            free(perm);
+            return 1;
+        }
+        for (f = 0; f < N; f++) {
+            memcpy(w_out + f * K, w + perm[f] * K, (size_t)K);
+            memcpy(codes_out + f * KB, codes + perm[f] * KB, (size_t)KB);
+        }
+    } else {
+        const int64_t crows = layout == ORC_BLK32 ? N / 32 : N;
+        if (K % heads != 0 || (layout == ORC_BLK32 && N % 32 != 0))
+            return 1;
+        perm = malloc((size_t)K * sizeof *perm);
+        if (orc_o_fused_perm(heads, K / heads, perm)) {
+            free(perm);
+            return 1;
+        }
+        for (n = 0; n < N; n++)
+            for (f = 0; f < K; f++)
+                w_out[n * K + f] = w[n * K + perm[f]];
+        for (n = 0; n < crows; n++)
+            for (f = 0; f < KB; f++)
+                codes_out[n * KB + f] = codes[n * KB + perm[32 * f] / 32];
+    }
+    free(perm);
+    return 0;
+}
+
 /* SiLU, v * sigmoid(v) = v / (1 + e^-v), in binary64.  The pages pair each
  * gate row with its up row (moe_copies) for the routed experts' up-gate
  * product; the gated activation they feed is read as SiLU, the activation of
