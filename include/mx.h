@@ -163,6 +163,28 @@ mx_status mx_e4m3_from_dequant(int layout, int64_t N, int64_t K, const void *w_b
                                int64_t ldw, const void *codes, void *w_out, void *ws,
                                size_t ws_bytes, mx_stream_t stream);
 
+/* Load-time permutations of an MXFP8 linear for an attention kernel's
+ * layouts ([fused_layout]: applied once to the weights, so the linear itself
+ * produces or consumes the kernel's layout).
+ *   kind MX_PERM_Q_ROWS ([fused_layout] permute_wq_b_, q_fused_permutation):
+ *     the weight's N = heads * D output rows, cut per head into 16-row chunks,
+ *     reordered chunk-major: output row (d / 16) heads 16 + h 16 + d % 16 is
+ *     input row h D + d; its ROW32 codes move with their rows (BLK32 codes
+ *     cannot: a 32-row block would hold two heads -> MX_ERR_UNSUPPORTED).
+ *     Rules: N % heads == 0, D % 16 == 0.
+ *   kind MX_PERM_O_COLS ([fused_layout] permute_wo_a_, o_fused_permutation):
+ *     the K = heads * D input columns (one group of heads), cut per head into
+ *     32-column chunks, reordered chunk-major: output column (c heads + h) 32
+ *     + j is input column h D + 32 c + j; each code column (ROW32 or BLK32)
+ *     moves with its 32-column chunk.  Rules: K % heads == 0, D % 32 == 0.
+ *   w, w_out       (device) E4M3 bytes [N, K], 16-byte aligned, distinct
+ *   codes, codes_out (device) ROW32 [N, K/32] or BLK32 [N/32, K/32]
+ * Out of place; pack the outputs with mx_pack_weights.  Asynchronous. */
+typedef enum { MX_PERM_Q_ROWS = 0, MX_PERM_O_COLS = 1 } mx_perm_kind;
+mx_status mx_fused_layout_permute(int kind, int layout, int64_t N, int64_t K, int64_t heads,
+                                  const void *w, const void *codes, void *w_out,
+                                  void *codes_out, mx_stream_t stream);
+
 /* Per-token MXFP8 activation quantization ([rocm_native] _quant_mxfp8_tile;
  * rule as in mx_quant_rule).
  *   x      (device) bf16 [M, ldx], 16-byte aligned, ldx % 8 == 0, ldx >= K

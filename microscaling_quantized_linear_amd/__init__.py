@@ -23,7 +23,8 @@ __all__ = [
     "mx_packed_sizes", "mx_pack_weights", "mx_quant_act", "mx_act_t16_sizes",
     "mx_quant_act_t16", "mx_linear_workspace",
     "mx_linear", "mx_moe_workspace", "mx_moe_linear", "mx_moe_copies", "mx_moe_gate_up",
-    "mx_moe_down", "mx_fold_row_codes", "mx_e4m3_from_dequant", "mx_set_batch_invariant", "mx_status_str",
+    "mx_moe_down", "mx_fold_row_codes", "mx_e4m3_from_dequant", "mx_set_batch_invariant",
+    "mx_fused_layout_permute", "MX_PERM_Q_ROWS", "MX_PERM_O_COLS", "mx_status_str",
     "mx_arch_supported",
 ]
 
@@ -31,6 +32,7 @@ MX_E4M3, MX_E2M1 = 0, 1
 MX_SCALE_ROW32, MX_SCALE_BLK32 = 0, 1
 MX_RULE_OCP, MX_RULE_CEIL448 = 0, 1
 MX_ACT_BF16, MX_ACT_MXFP8, MX_ACT_MXFP8_T16 = 0, 1, 2
+MX_PERM_Q_ROWS, MX_PERM_O_COLS = 0, 1
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmx.so")
 _lib = None
@@ -75,11 +77,12 @@ def lib() -> C.CDLL:
         L.mx_set_batch_invariant.argtypes = [i32]
         L.mx_set_batch_invariant.restype = i32
         L.mx_fold_row_codes.argtypes = [i64, i64, p, i64, p, p, sz, p]
+        L.mx_fused_layout_permute.argtypes = [i32, i32, i64, i64, i64, p, p, p, p, p]
         L.mx_e4m3_from_dequant.argtypes = [i32, i64, i64, p, i64, p, p, p, sz, p]
         for name in ("mx_packed_sizes", "mx_pack_weights", "mx_quant_act", "mx_act_t16_sizes",
                      "mx_quant_act_t16", "mx_linear_workspace", "mx_linear", "mx_moe_workspace",
                      "mx_moe_linear", "mx_moe_copies", "mx_moe_gate_up", "mx_moe_down",
-                     "mx_fold_row_codes", "mx_e4m3_from_dequant"):
+                     "mx_fold_row_codes", "mx_e4m3_from_dequant", "mx_fused_layout_permute"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -209,3 +212,9 @@ def mx_e4m3_from_dequant(layout, N, K, w_bf16, ldw, codes, w_out, ws, ws_bytes, 
 def mx_set_batch_invariant(on: bool) -> bool:
     """Turn the process-wide batch-invariant mode on or off; the previous setting."""
     return bool(lib().mx_set_batch_invariant(1 if on else 0))
+
+
+def mx_fused_layout_permute(kind, layout, N, K, heads, w, codes, w_out, codes_out, stream=None):
+    _check(lib().mx_fused_layout_permute(kind, layout, N, K, heads, _ptr(w), _ptr(codes),
+                                         _ptr(w_out), _ptr(codes_out), _stream(stream)),
+           "mx_fused_layout_permute")

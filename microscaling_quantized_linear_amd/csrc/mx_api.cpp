@@ -529,6 +529,25 @@ mx_status mx_fold_row_codes(int64_t N, int64_t K, const void *codes_row, int64_t
     });
 }
 
+mx_status mx_fused_layout_permute(int kind, int layout, int64_t N, int64_t K, int64_t heads,
+                                  const void *w, const void *codes, void *w_out,
+                                  void *codes_out, mx_stream_t stream) {
+    if (kind != 0 && kind != 1) return MX_ERR_UNSUPPORTED;
+    if (layout != ROW32 && layout != BLK32) return MX_ERR_UNSUPPORTED;
+    if (kind == 0 && layout != ROW32) return MX_ERR_UNSUPPORTED;
+    if (N < 1 || K < 32 || K % 32 != 0 || heads < 1) return MX_ERR_SHAPE;
+    if (kind == 0 && (N % heads != 0 || (N / heads) % 16 != 0)) return MX_ERR_SHAPE;
+    if (kind == 1 && (K % heads != 0 || (K / heads) % 32 != 0)) return MX_ERR_SHAPE;
+    if (layout == BLK32 && N % 32 != 0) return MX_ERR_SHAPE;
+    if (!w || !codes || !w_out || !codes_out) return MX_ERR_NULL;
+    if (!aligned16(w) || !aligned16(w_out)) return MX_ERR_ALIGN;
+    mx_status st = device_ok();
+    if (st != MX_OK) return st;
+    const int64_t crows = layout == BLK32 ? N / 32 : N;
+    return launched(mx::launch_fused_layout(kind, N, K, heads, crows, w, codes, w_out, codes_out,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
 mx_status mx_e4m3_from_dequant(int layout, int64_t N, int64_t K, const void *w_bf16,
                                int64_t ldw, const void *codes, void *w_out, void *ws,
                                size_t ws_bytes, mx_stream_t stream) {

@@ -10,6 +10,10 @@
 // dequantized e4m3 weights to bf16 (w = e4m3 x 2^(code - 127)) hands back
 // bf16; the e4m3 byte is rebuilt from w's exponent and mantissa fields with
 // integer arithmetic, and a weight no byte reproduces exactly is marked 0xFF.
+//
+// fused_q_rows_kernel, fused_o_cols_kernel ([fused_layout] permute_wq_b_,
+// permute_wo_a_): an attention kernel's Q and O layouts applied once to the
+// rows or input columns of the linears around it, codes moving with them.
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -86,6 +90,47 @@ __global__ void __launch_bounds__(256) e4m3_from_bf16_kernel(
     if (any) atomicOr(bad, 1);
 }
 
+// [fused_layout] permute_wq_b_: output row f of the Q layout is standard row
+// h D + d with f = (d / 16) H 16 + h 16 + d % 16; whole rows move, with their
+// per-row codes.  One thread per 16-byte piece of a row, then per code byte.
+__global__ void __launch_bounds__(256) fused_q_rows_kernel(
+    int64_t N, int64_t K, int64_t H, const v4u *__restrict__ w,
+    const uint8_t *__restrict__ codes, v4u *__restrict__ wo, uint8_t *__restrict__ co) {
+    const int64_t D = N / H, P = K / 16, KB = K / 32;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < N * (P + KB);
+         q += (int64_t)gridDim.x * blockDim.x) {
+        const bool piece = q < N * P;
+        const int64_t per = piece ? P : KB, qq = piece ? q : q - N * P;
+        const int64_t f = qq / per, b = qq % per;
+        const int64_t chunk = f / (H * 16), rem = f % (H * 16);
+        const int64_t src = (rem / 16) * D + chunk * 16 + rem % 16;
+        if (piece)
+            wo[f * P + b] = w[src * P + b];
+        else
+            co[f * KB + b] = codes[src * KB + b];
+    }
+}
+
+// [fused_layout] permute_wo_a_: output column chunk fc = c G + h (32 columns)
+// is standard chunk h (D / 32) + c; each code column moves with its chunk.
+__global__ void __launch_bounds__(256) fused_o_cols_kernel(
+    int64_t N, int64_t K, int64_t G, int64_t crows, const v4u *__restrict__ w,
+    const uint8_t *__restrict__ codes, v4u *__restrict__ wo, uint8_t *__restrict__ co) {
+    const int64_t C = K / 32 / G, P = K / 16, KB = K / 32;
+    for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < N * P + crows * KB;
+         q += (int64_t)gridDim.x * blockDim.x) {
+        const bool piece = q < N * P;
+        const int64_t qq = piece ? q : q - N * P;
+        const int64_t per = piece ? P : KB, n = qq / per, b = qq % per;
+        const int64_t fc = piece ? b / 2 : b;
+        const int64_t sc = (fc % G) * C + fc / G;        // standard chunk
+        if (piece)
+            wo[n * P + b] = w[n * P + 2 * sc + b % 2];
+        else
+            co[n * KB + b] = codes[n * KB + sc];
+    }
+}
+
 static unsigned ingest_grid(int64_t n) {
     const int64_t g = (n + 255) / 256;
     return (unsigned)(g < 1 ? 1 : (g > 16384 ? 16384 : g));
@@ -103,6 +148,21 @@ hipError_t launch_e4m3_from_bf16(int layout, int64_t N, int64_t K, const void *w
     hipLaunchKernelGGL(e4m3_from_bf16_kernel, dim3(ingest_grid(N * (K / 8))), dim3(256), 0, st,
                        layout, N, K, (const uint16_t *)w, ldw, (const uint8_t *)codes,
                        (uint8_t *)out, bad);
+    return hipGetLastError();
+}
+
+hipError_t launch_fused_layout(int kind, int64_t N, int64_t K, int64_t heads, int64_t crows,
+                               const void *w, const void *codes, void *wo, void *co,
+                               hipStream_t st) {
+    if (kind == 0)
+        hipLaunchKernelGGL(fused_q_rows_kernel, dim3(ingest_grid(N * (K / 16 + K / 32))),
+                           dim3(256), 0, st, N, K, heads, (const v4u *)w, (const uint8_t *)codes,
+                           (v4u *)wo, (uint8_t *)co);
+    else
+        hipLaunchKernelGGL(fused_o_cols_kernel,
+                           dim3(ingest_grid(N * (K / 16) + crows * (K / 32))), dim3(256), 0, st,
+                           N, K, heads, crows, (const v4u *)w, (const uint8_t *)codes, (v4u *)wo,
+                           (uint8_t *)co);
     return hipGetLastError();
 }
 

@@ -66,6 +66,9 @@ hipError_t launch_moe_copies(int elem, int64_t E, int64_t Np, int64_t inter, int
                              int64_t H, const void *w13, const void *s13, const void *w2,
                              const void *s2, void *ow13, void *os13, void *ow2, void *os2,
                              hipStream_t stream);
+hipError_t launch_fused_layout(int kind, int64_t N, int64_t K, int64_t heads, int64_t crows,
+                               const void *w, const void *codes, void *wo, void *co,
+                               hipStream_t st);
 hipError_t launch_fold_codes(int64_t N, int64_t KB, int64_t ldc, const void *in, void *out,
                              int *bad, hipStream_t st);
 hipError_t launch_e4m3_from_bf16(int layout, int64_t N, int64_t K, const void *w, int64_t ldw,

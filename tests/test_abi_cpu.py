@@ -259,6 +259,27 @@ def test_batch_invariant_switch_and_workspace():
         mx.mx_set_batch_invariant(prev)
 
 
+def test_fused_layout_validation_paths():
+    L = mx.lib()
+
+    def perm(**kw):
+        a = dict(kind=0, layout=0, N=128, K=256, heads=4, out=A)
+        a.update(kw)
+        return L.mx_fused_layout_permute(a["kind"], a["layout"], a["N"], a["K"], a["heads"], A,
+                                         A, a["out"], A, None)
+    assert perm(kind=2) == UNSUP
+    assert perm(layout=1) == UNSUP           # Q rows need per-row codes
+    assert perm(heads=3) == SHAPE            # N % heads
+    assert perm(N=96, heads=4) == SHAPE      # D = 24: not a multiple of 16
+    assert perm(kind=1, heads=16) == SHAPE   # D = 16: not a multiple of 32
+    assert perm(kind=1, layout=1, N=48, heads=4) == SHAPE
+    assert perm(K=100) == SHAPE
+    assert perm(out=None) == NULL
+    import torch
+    if not torch.cuda.is_available():
+        assert perm() == DEVICE and perm(kind=1, layout=1) == DEVICE
+
+
 def test_binding_raises_without_touching_the_device():
     with pytest.raises(mx.MXError) as ei:
         mx.mx_packed_sizes(0, 0, 1, 24, 512)

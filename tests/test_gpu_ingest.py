@@ -1,7 +1,8 @@
-"""Parity of the ingest entry points (mx_fold_row_codes, mx_e4m3_from_dequant)
-with the oracle, through the C ABI: bytes and status bit for bit, including
-the 0xFF markers of weights that are not recovered; then the whole ingest
-chain (fold, pack, linear) at the 7168 x 7168 decode shape."""
+"""Parity of the ingest entry points (mx_fold_row_codes, mx_e4m3_from_dequant,
+mx_fused_layout_permute) with the oracle, through the C ABI: bytes and
+status bit for bit, including the 0xFF markers of weights that are not
+recovered; then the whole ingest chain (fold, pack, linear) at the
+7168 x 7168 decode shape, and the linear over permuted weights."""
 import numpy as np
 import pytest
 
@@ -170,3 +171,61 @@ def test_ingest_chain_at_decode_shape(g):
                               np.arange(16).repeat(8), np.arange(0, N, 56)[:128], x=d["x"])
     g.assert_close(ys[0][np.arange(16).repeat(8), np.arange(0, N, 56)[:128]], ref,
                    "ingest chain")
+
+
+# ------------------------------------------------------------------ attention layouts
+
+def _permute(g, kind, layout, N, K, heads, w, codes):
+    import torch
+    import microscaling_quantized_linear_amd as mx
+    wo = torch.full((N, K), 0xAB, dtype=torch.uint8, device=g.DEV)
+    co = torch.full(codes.shape, 0xAB, dtype=torch.uint8, device=g.DEV)
+    mx.mx_fused_layout_permute(kind, layout, N, K, heads, g.dev(w), g.dev(codes), wo, co)
+    torch.cuda.synchronize()
+    return wo.cpu().numpy(), co.cpu().numpy()
+
+
+@pytest.mark.parametrize("heads,D,K", [(4, 32, 96), (2, 64, 160), (16, 192, 1536)])
+def test_q_rows_permute(g, heads, D, K):
+    """Bytes and codes equal the oracle's; the linear over the permuted
+    weight gives the standard output's columns in the Q layout, bit for bit
+    (the same sums), for the W8A8 and the A16 GEMV."""
+    rng = np.random.default_rng([121, heads, D, K])
+    N = heads * D
+    w = wl.e4m3_bytes(rng, (N, K))
+    codes = wl.codes(rng, (N, K // 32), 118, 134)
+    wq, cq = _permute(g, 0, ROW32, N, K, heads, w, codes)
+    ow, oc = oracle.fused_layout_permute(0, ROW32, N, K, heads, w, codes)
+    np.testing.assert_array_equal(wq, ow)
+    np.testing.assert_array_equal(cq, oc)
+    perm = oracle.q_fused_perm(heads, D)
+    x = wl.activations(rng, (16, K))
+    wp, cp = g.pack(E4M3, ROW32, 1, N, K, w, codes)
+    wpq, cpq = g.pack(E4M3, ROW32, 1, N, K, wq, cq)
+    for act in (BF16, 1):
+        y = g.linear(E4M3, ROW32, N, K, wp, cp, act, x=x)
+        yq = g.linear(E4M3, ROW32, N, K, wpq, cpq, act, x=x)
+        np.testing.assert_array_equal(yq, y[:, perm])
+
+
+@pytest.mark.parametrize("layout,G,D,N", [(ROW32, 8, 64, 48), (BLK32, 4, 128, 64),
+                                          (BLK32, 8, 512, 1024)])
+def test_o_cols_permute(g, layout, G, D, N):
+    """Bytes and codes equal the oracle's; the linear over the permuted
+    weight, fed the activation in the O layout, meets the bar against the
+    oracle's standard product."""
+    rng = np.random.default_rng([122, layout, G, D, N])
+    K = G * D
+    w = wl.e4m3_bytes(rng, (N, K))
+    codes = wl.codes(rng, (N // 32 if layout == BLK32 else N, K // 32), 118, 134)
+    wo, co = _permute(g, 1, layout, N, K, G, w, codes)
+    ow, oc = oracle.fused_layout_permute(1, layout, N, K, G, w, codes)
+    np.testing.assert_array_equal(wo, ow)
+    np.testing.assert_array_equal(co, oc)
+    perm = oracle.o_fused_perm(G, D)
+    x = wl.activations(rng, (8, K))
+    xf = np.ascontiguousarray(x[:, perm])
+    wpo, cpo = g.pack(E4M3, layout, 1, N, K, wo, co)
+    yo = g.linear(E4M3, layout, N, K, wpo, cpo, BF16, x=xf)
+    ref = oracle.linear(E4M3, layout, N, K, w, codes.reshape(-1), 8, BF16, x=x)
+    g.assert_close(yo, ref, "o layout")
