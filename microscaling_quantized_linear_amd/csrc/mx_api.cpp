@@ -236,7 +236,7 @@ mx_status mx_packed_sizes(int elem, int layout, int64_t E, int64_t N, int64_t K,
     mx_status st = shape_ok(elem, layout, E, N, K);
     if (st != MX_OK) return st;
     const int64_t Kp = padded_k(K), S = Kp / 128, Q = (S + 3) / 4;
-    *w_bytes = (size_t)(E * N * (elem == E4M3 ? Kp : Kp / 2));
+    *w_bytes = (size_t)(E * N * (elem == E4M3 ? K : K / 2));   // no stored padding
     *code_bytes = (size_t)(layout == ROW32 ? E * (N / 16) * Q * 256 : E * (N / 32) * Q * 16);
     return MX_OK;
 }

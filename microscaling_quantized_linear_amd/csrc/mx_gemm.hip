@@ -39,7 +39,10 @@ constexpr int kBM = 256;           // tokens per workgroup
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int LAYOUT, int NTW>
+// TAIL: K % 128 != 0, the last step's chunks are cut to their valid prefix
+// (instantiated apart so the steady-state copies of whole-step shapes carry
+// no extra mask)
+template <int LAYOUT, int NTW, bool TAIL>
 __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     constexpr int BN = NTW * 32;
     constexpr int kWBytes = 2 * NTW * 2048;               // one step's weight chunks
@@ -73,8 +76,12 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     const int64_t t0 = n0 / 16;                           // first weight tile
     const int64_t mbw = m0 / 16 + 4 * wave;               // this wavefront's first token tile
 
+    // a weight tile is 16 K bytes: S - 1 whole chunks, then the last step's
+    // valid prefix of tailb bytes (no padding stored)
+    const int64_t TILEB = 16 * p.K;
+    const uint32_t tailb = (uint32_t)(TILEB - (S - 1) * 2048);
     const __amdgpu_buffer_rsrc_t wr =
-        make_rsrc(p.w + t0 * S * 2048, (uint32_t)((T - t0) * S * 2048));
+        make_rsrc(p.w + t0 * TILEB, (uint32_t)((T - t0) * TILEB));
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.xq, (uint32_t)(MB * S * 2048));
     const __amdgpu_buffer_rsrc_t xcr = make_rsrc(p.xct, (uint32_t)act_codes_t16_bytes(p.M, p.K));
     const __amdgpu_buffer_rsrc_t cr =
@@ -85,16 +92,21 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     // the step (NTW of them); chunk-half i = 2 c + h lands at i KB.  Offsets
     // of out-of-range loads get bit 31 set (every resource is below 2 GiB, so
     // those lanes read zeros); no branches in the loop body.
-    uint32_t wofs[NTW];
+    // (wtail: the piece lies past the valid prefix of the last step's chunk)
+    uint32_t wofs[NTW], wtail[NTW];
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
         const int idx = wave + 4 * i, c = idx / 2, h = idx % 2;
-        wofs[i] = t0 + c < T ? (uint32_t)(c * S * 2048 + 1024 * h + 16 * lane) : kOOB;
+        const uint32_t o = (uint32_t)(1024 * h + 16 * lane);
+        wofs[i] = t0 + c < T ? (uint32_t)(c * TILEB) + o : kOOB;
+        wtail[i] = o >= tailb ? kOOB : 0u;
     }
     auto dma_one = [&](uint8_t *buf, int s, int i) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             wr, (lds_void *)(buf + (wave + 4 * i) * 1024), 16,
-            (int)((wofs[i] + (uint32_t)s * 2048u) | (s >= S ? kOOB : 0u)), 0, 0, 0);
+            (int)((wofs[i] + (uint32_t)s * 2048u) | (s >= S ? kOOB : 0u) |
+                  (TAIL && s == S - 1 ? wtail[i] : 0u)),
+            0, 0, 0);
     };
 
     // ---- 32 x 32 x 64 operands: lane (g, rr) = lane / 32, lane % 32 holds
@@ -364,8 +376,12 @@ template <int LAYOUT, int NTW>
 static hipError_t launch_ntw(const GemmArgs &a, hipStream_t st) {
     constexpr int BN = NTW * 32;
     const int64_t tiles = ((a.N + BN - 1) / BN) * ((a.M + kBM - 1) / kBM);
-    hipLaunchKernelGGL((gemm_w8a8_kernel<LAYOUT, NTW>), dim3((unsigned)tiles), dim3(256), 0, st,
-                       a);
+    if (a.K % 128 != 0)
+        hipLaunchKernelGGL((gemm_w8a8_kernel<LAYOUT, NTW, true>), dim3((unsigned)tiles),
+                           dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((gemm_w8a8_kernel<LAYOUT, NTW, false>), dim3((unsigned)tiles),
+                           dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

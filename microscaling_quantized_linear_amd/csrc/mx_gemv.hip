@@ -101,8 +101,12 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
     }
 
     // resources: the group's weight chunks, codes, the activations
+    // a tile is 16 row lengths: S - 1 whole chunks, then the last step's
+    // valid prefix of tailb bytes (no padding stored)
+    const int64_t TILEB = 16 * (ELEM == E4M3 ? p.K : p.K / 2);
+    const uint32_t tailb = (uint32_t)(TILEB - (S - 1) * CHUNK);
     const __amdgpu_buffer_rsrc_t wr =
-        make_rsrc(p.w + (e * T + t0) * S * CHUNK, (uint32_t)(ntiles * S * CHUNK));
+        make_rsrc(p.w + (e * T + t0) * TILEB, (uint32_t)(ntiles * TILEB));
     __amdgpu_buffer_rsrc_t cr;
     if (LAYOUT == ROW32)
         cr = make_rsrc(p.codes + (e * T + t0) * Q * 256, (uint32_t)(ntiles * Q * 256));
@@ -120,9 +124,13 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
     const int64_t batches = (nslots + 15) / 16;
     const int64_t b_first = MOE ? 0 : blockIdx.y, b_last = MOE ? batches : blockIdx.y + 1;
 
-    // weight and code offsets of tile g at step s (out of range beyond s1)
-    auto woff = [&](int g, int64_t s, bool in) -> uint32_t {
-        return in ? (uint32_t)((g * S + s) * CHUNK + 16 * lane) : kOOB;
+    // weight and code offsets of tile g at step s (out of range beyond s1,
+    // and past the last step's valid prefix); half 1 is an E4M3 chunk's
+    // second 1 KB
+    auto woff = [&](int g, int64_t s, bool in, int half) -> uint32_t {
+        const uint32_t o = (uint32_t)(1024 * half + 16 * lane);
+        if (!in || (s == S - 1 && o >= tailb)) return kOOB;
+        return (uint32_t)(g * TILEB + s * CHUNK) + o;
     };
     // the dword holding this step's code of the lane's row for lane group jj
     // (byte s % 4 of it): ROW32 the lane's own C-T16 dword, BLK32 dword jj of
@@ -163,9 +171,8 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
                 const bool in = s < s1;
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
-                    const uint32_t wo = woff(g, s, in);
-                    st.a0[g] = load16<kNT>(wr, wo);
-                    st.a1[g] = load16<kNT>(wr, in ? wo + 1024u : kOOB);
+                    st.a0[g] = load16<kNT>(wr, woff(g, s, in, 0));
+                    st.a1[g] = load16<kNT>(wr, woff(g, s, in, 1));
                 }
                 const int64_t k0 = 128 * s + 16 * j, k1 = k0 + 64;   // K of each 16-byte half
                 st.b0 = load16(xr, in && live && k0 < p.K ? xbase + (uint32_t)k0 : kOOB);
@@ -204,9 +211,8 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
                 if (ELEM == E4M3) {
 #pragma unroll
                     for (int g = 0; g < G; ++g) {
-                        const uint32_t wo = woff(g, s, in);
-                        st.a0[g] = load16<kNT>(wr, wo);
-                        st.a1[g] = load16<kNT>(wr, in ? wo + 1024u : kOOB);
+                        st.a0[g] = load16<kNT>(wr, woff(g, s, in, 0));
+                        st.a1[g] = load16<kNT>(wr, woff(g, s, in, 1));
                     }
                     // MFMA d covers K 16 j + 8 d (d < 2) and 64 + 16 j + 8 (d - 2)
                     const int64_t k0 = 128 * s + 16 * j, k1 = k0 + 64;
@@ -217,7 +223,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_kernel(GemvArgs p) {
                     st.x3 = load16(xr, v1 ? xbase + (uint32_t)(2 * k1 + 16) : kOOB);
                 } else {
 #pragma unroll
-                    for (int g = 0; g < G; ++g) st.a0[g] = load16<kNT>(wr, woff(g, s, in));
+                    for (int g = 0; g < G; ++g) st.a0[g] = load16<kNT>(wr, woff(g, s, in, 0));
                     const int64_t k0 = 128 * s + 32 * j;            // the lane's whole block
                     const bool v0 = in && live && k0 < p.K;
                     st.x0 = load16(xr, v0 ? xbase + (uint32_t)(2 * k0) : kOOB);

@@ -129,18 +129,23 @@ __global__ void __launch_bounds__(512) gemv_w8_kernel(GemvW8Args p) {
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 3. every weight chunk of the range ----
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w + t0 * S * 2048, (uint32_t)(ntiles * S * 2048));
+    // a tile is 16 K bytes: S - 1 whole chunks, then the last step's valid
+    // prefix of tailb bytes (no padding stored)
+    const int64_t TILEB = 16 * p.K;
+    const uint32_t tailb = (uint32_t)(TILEB - (S - 1) * 2048);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w + t0 * TILEB, (uint32_t)(ntiles * TILEB));
     v4u wv[SPW][G][2];
 #pragma unroll
     for (int i = 0; i < SPW; ++i)
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const uint32_t base = i < n && g < ntiles
-                                      ? (uint32_t)((g * S + s0 + i) * 2048 + 16 * lane)
-                                      : kOOB;
-            wv[i][g][0] = load16<kNT>(wr, base);
-            wv[i][g][1] = load16<kNT>(wr, base == kOOB ? kOOB : base + 1024u);
-        }
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int64_t s = s0 + i;
+                const uint32_t o = (uint32_t)(1024 * h + 16 * lane);
+                const bool in = i < n && g < ntiles && (s < S - 1 || o < tailb);
+                wv[i][g][h] = load16<kNT>(wr, in ? (uint32_t)(g * TILEB + s * 2048) + o : kOOB);
+            }
     __builtin_amdgcn_sched_barrier(0);
 
     // The copies into LDS were issued before every other load of this
@@ -547,9 +552,10 @@ static hipError_t even_dispatch(const GemvW8Plan &pl, F &&f) {
     }
 }
 
+// (K % 128 == 0: the even kernels step through whole 2 KB chunks, S per tile)
 bool gemv_w8_even(int64_t N, int64_t K, const GemvW8Plan &pl) {
-    const int64_t S = (K + 127) / 128, T = N / 16;
-    return pl.ok && pl.nw == 8 && S == 8 * (int64_t)pl.spw && T % pl.g == 0 &&
+    const int64_t S = K / 128, T = N / 16;
+    return K % 128 == 0 && pl.ok && pl.nw == 8 && S == 8 * (int64_t)pl.spw && T % pl.g == 0 &&
            pl.g * pl.spw <= 16;
 }
 

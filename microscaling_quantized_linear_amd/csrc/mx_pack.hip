@@ -6,43 +6,45 @@
 // wavefront reading 1 KB that is contiguous); the code staging follows
 // [weights942] codes_tile_rounds (a lane group reads its rows' codes from one
 // line) with the per-lane dwords of [a16w4] scale_loads; BLK32 codes get the
-// same dword-per-lane-group, byte-per-step staging.  Padding to
-// Kp = 128 * ceil(K / 128) uses zero bytes and code 128 ([weights942]
-// dense_copy).
+// same dword-per-lane-group, byte-per-step staging.  Codes are padded to
+// Kp = 128 * ceil(K / 128) with code 128 ([weights942] dense_copy pads its
+// steps); weights store no padding: the valid bytes of a K % 128 tail step
+// are a prefix of its chunk, and the chunk is stored cut to them, so a tile
+// is exactly 16 row lengths.
 #include "mx_device.h"
 #include "mx_kernels.h"
 
 namespace mx {
 
 // One thread writes one 16-byte piece of the packed weights (a gather: every
-// destination piece is read from exactly one source piece, or zero-filled).
+// destination piece is read from exactly one source piece).  A tile holds
+// 16 row lengths of bytes; piece o of it is in chunk o / CHUNK.
 __global__ void __launch_bounds__(256) pack_weights_kernel(
     int elem, int64_t E, int64_t N, int64_t K, const uint8_t *__restrict__ w,
     uint8_t *__restrict__ wp, int64_t npieces) {
     int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (p >= npieces) return;
-    const int64_t Kp = (K + 127) / 128 * 128, S = Kp / 128, T = N / 16;
+    const int64_t T = N / 16;
     const int64_t row_bytes = elem == E4M3 ? K : K / 2;
-    int64_t chunk, lane, h, kbyte;
+    const int64_t tile_pieces = row_bytes;                 // 16 rows x row_bytes / 16
+    const int64_t et = p / tile_pieces, o = p % tile_pieces;   // et = e * T + t
+    int64_t s, lane, kbyte;
     if (elem == E4M3) {             // 128 pieces per 2 KB chunk
-        chunk = p / 128;
-        h = (p % 128) / 64;
-        lane = p % 64;
+        s = o / 128;
+        const int64_t h = (o % 128) / 64;
+        lane = o % 64;
         kbyte = 64 * h + 16 * (lane / 16);
     } else {                        // 64 pieces per 1 KB chunk
-        chunk = p / 64;
-        lane = p % 64;
+        s = o / 64;
+        lane = o % 64;
         kbyte = 16 * (lane / 16);
     }
-    const int64_t s = chunk % S, et = chunk / S;          // et = e * T + t
     const int64_t e = et / T, t = et % T;
     const int64_t row = e * N + 16 * t + lane % 16;
     const int64_t step_bytes = elem == E4M3 ? 128 : 64;
-    const int64_t off = s * step_bytes + kbyte;           // byte within the row
-    v4u v = {0u, 0u, 0u, 0u};
-    if (off < row_bytes)                                   // K % 32 == 0: whole piece in or out
-        v = *reinterpret_cast<const v4u *>(w + row * row_bytes + off);
-    *reinterpret_cast<v4u *>(wp + p * 16) = v;
+    const int64_t off = s * step_bytes + kbyte;           // byte within the row, < row_bytes
+    *reinterpret_cast<v4u *>(wp + p * 16) =
+        *reinterpret_cast<const v4u *>(w + row * row_bytes + off);
 }
 
 // ROW32: one thread writes one dword (4 codes) of C-T16.  BLK32: one byte.
@@ -146,7 +148,7 @@ hipError_t launch_act_data_t16(int64_t M, int64_t K, const void *xq, int64_t ldq
 hipError_t launch_pack(int elem, int layout, int64_t E, int64_t N, int64_t K, const void *w,
                        const void *codes, void *wp, void *cp, int *bad, hipStream_t stream) {
     const int64_t Kp = (K + 127) / 128 * 128, S = Kp / 128, Q = (S + 3) / 4;
-    const int64_t wbytes = E * N * (elem == E4M3 ? Kp : Kp / 2);
+    const int64_t wbytes = E * N * (elem == E4M3 ? K : K / 2);
     const int64_t npieces = wbytes / 16;
     hipLaunchKernelGGL(pack_weights_kernel, dim3((unsigned)((npieces + 255) / 256)), dim3(256), 0,
                        stream, elem, E, N, K, (const uint8_t *)w, (uint8_t *)wp, npieces);

@@ -227,7 +227,11 @@ void orc_quant_act(int64_t M, int64_t K, const uint16_t *x, int64_t ldx,
  * 128 K values: 2048 bytes for E4M3, 1024 for E2M1.  Lane l reads 16-byte
  * pieces at 16 l (+ 1024 for the second E4M3 half), so every 16-byte load of
  * the wavefront reads 1 KB contiguous: the tile-major idea of [weights942]
- * dense_copy and fp4_tile_major.  Padding bytes are 0.
+ * dense_copy and fp4_tile_major.  When K % 128 != 0 the last step holds
+ * TB = (K % 128) / 32 blocks; its valid bytes are exactly the first TB * 512
+ * (E4M3) or TB * 256 (E2M1) bytes of the chunk, and the chunk is stored cut
+ * to them, so a tile takes exactly 16 row lengths of bytes, TILEB = 16 K
+ * (E4M3) or 8 K (E2M1): no padding is stored (reading R21).
  *   E4M3: lane l holds row 16 t + r, K 16 j .. 16 j + 15 of the step in its
  *         first half and K 64 + 16 j .. + 15 in its second half -- the K
  *         order in which a gfx950 16x16x128 scaled matrix-core operand lane
@@ -235,10 +239,11 @@ void orc_quant_act(int64_t M, int64_t K, const uint16_t *x, int64_t ldx,
  *   E2M1: lane l holds row 16 t + r, the whole 32-value block 4 s + j (one
  *         code group a lane), as in [a16w4] (module notes).
  *
- *   E4M3: wp[((e T + t) S + s) 2048 + 1024 h + 16 l + c]
- *           = w[e][16 t + r][128 s + 64 h + 16 j + c]
- *   E2M1: wp[((e T + t) S + s) 1024 + 16 l + c]
- *           = w[e][16 t + r][byte 64 s + 16 j + c]       (low nibble = even K)
+ *   E4M3: wp[(e T + t) TILEB + 2048 s + 1024 h + 16 l + c]
+ *           = w[e][16 t + r][128 s + 64 h + 16 j + c]      for K index < K
+ *   E2M1: wp[(e T + t) TILEB + 1024 s + 16 l + c]
+ *           = w[e][16 t + r][byte 64 s + 16 j + c]         for byte < K / 2
+ *                                                      (low nibble = even K)
  *
  * Codes ROW32 ([E N, K/32] in) -> C-T16.  For each (expert, tile, quad) 256
  * bytes; lane l's dword holds the codes of its row for the blocks it owns in
@@ -269,7 +274,8 @@ int orc_packed_sizes(int elem, int layout, int64_t E, int64_t N, int64_t K,
         return 1;
     if (layout == ORC_BLK32 && N % 32 != 0)
         return 1;
-    *w_bytes = E * N * (elem == ORC_E4M3 ? Kp : Kp / 2);
+    *w_bytes = E * N * (elem == ORC_E4M3 ? K : K / 2);          /* no stored padding */
+    (void)Kp;
     if (layout == ORC_ROW32)
         *c_bytes = E * (N / 16) * Q * 256;
     else
@@ -282,6 +288,7 @@ int orc_pack_weights(int elem, int layout, int64_t E, int64_t N, int64_t K,
                      uint8_t *cp)
 {
     int64_t Kp = orc_padded_k(K), S = Kp / 128, Q = (S + 3) / 4, T = N / 16;
+    int64_t tileb = 16 * (elem == ORC_E4M3 ? K : K / 2);
     int64_t wb, cb, e, t, s, q, l, h, c, u;
     if (orc_packed_sizes(elem, layout, E, N, K, &wb, &cb))
         return 1;
@@ -294,14 +301,16 @@ int orc_pack_weights(int elem, int layout, int64_t E, int64_t N, int64_t K,
                         for (h = 0; h < 2; h++)
                             for (c = 0; c < 16; c++) {
                                 int64_t k = 128 * s + 64 * h + 16 * j + c;
-                                int64_t dst = ((e * T + t) * S + s) * 2048 + 1024 * h + 16 * l + c;
-                                wp[dst] = k < K ? w[(e * N + row) * K + k] : 0;
+                                int64_t dst = (e * T + t) * tileb + 2048 * s + 1024 * h + 16 * l + c;
+                                if (k < K)
+                                    wp[dst] = w[(e * N + row) * K + k];
                             }
                     } else {
                         for (c = 0; c < 16; c++) {
                             int64_t byte = 64 * s + 16 * j + c;
-                            int64_t dst = ((e * T + t) * S + s) * 1024 + 16 * l + c;
-                            wp[dst] = byte < K / 2 ? w[(e * N + row) * (K / 2) + byte] : 0;
+                            int64_t dst = (e * T + t) * tileb + 1024 * s + 16 * l + c;
+                            if (byte < K / 2)
+                                wp[dst] = w[(e * N + row) * (K / 2) + byte];
                         }
                     }
                 }

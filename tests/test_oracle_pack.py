@@ -4,10 +4,12 @@ The oracle writes each pack as a loop over destination offsets.  Here the same
 layouts are stated a second, independent way -- as numpy reshape/transpose of
 the padded standard tensors, the style in which the pages state their own
 repacks (vllm.models.deepseek_v41.amd.mono.weights942: dense_copy,
-fp4_tile_major, codes_tile_rounds) -- and the packs are checked to be
-permutations of the padded input (packed = standard[perm], the identity that
-vllm.models.deepseek_v41.common.ops.fused_layout builds its permutations on),
-with zero padding bytes and padding code 128.
+fp4_tile_major, codes_tile_rounds), with each tile's bytes then cut to 16 row
+lengths (the padding of a K % 128 tail sits past the valid prefix of the
+tile's last chunk and is not stored) -- and the weight pack is checked to be
+a permutation of the unpadded input (packed = standard[perm], the identity
+that vllm.models.deepseek_v41.common.ops.fused_layout builds its
+permutations on), the codes to carry padding code 128.
 """
 import numpy as np
 import pytest
@@ -29,9 +31,16 @@ def _ref_weights(elem, E, N, K, w):
     S, T = Kp // 128, N // 16
     if elem == E4M3:
         v = _pad_cols(w.reshape(E, N, K), Kp, 0).reshape(E, T, 16, S, 2, 4, 16)
-        return v.transpose(0, 1, 3, 4, 5, 2, 6).reshape(-1)   # [e,t,s,h,j,r,c]
-    v = _pad_cols(w.reshape(E, N, K // 2), Kp // 2, 0).reshape(E, T, 16, S, 4, 16)
-    return v.transpose(0, 1, 3, 4, 2, 5).reshape(-1)          # [e,t,s,j,r,c]
+        v = v.transpose(0, 1, 3, 4, 5, 2, 6)                  # [e,t,s,h,j,r,c]
+        tileb = 16 * K
+    else:
+        v = _pad_cols(w.reshape(E, N, K // 2), Kp // 2, 0).reshape(E, T, 16, S, 4, 16)
+        v = v.transpose(0, 1, 3, 4, 2, 5)                     # [e,t,s,j,r,c]
+        tileb = 8 * K
+    # per tile, the padded bytes all lie past the first 16 row lengths
+    v = v.reshape(E * T, -1)
+    assert not v[:, tileb:].any() or K % 128 == 0
+    return np.ascontiguousarray(v[:, :tileb]).reshape(-1)
 
 
 def _ref_codes(layout, E, N, K, codes):
@@ -73,16 +82,19 @@ def _labels(n):
     return [((idx >> (8 * p)) & 0xFF).astype(np.uint8) for p in range(3)]
 
 
-@pytest.mark.parametrize("elem", [E4M3, E2M1])
-def test_weight_pack_is_a_permutation(elem):
-    # K a multiple of 128: no padding, so the pack must be a bijection
-    E, N, K = 2, 32, 256
+@pytest.mark.parametrize("elem,K", [(E4M3, 256), (E2M1, 256), (E4M3, 160), (E4M3, 224),
+                                    (E4M3, 192), (E2M1, 160), (E2M1, 224)])
+def test_weight_pack_is_a_permutation(elem, K):
+    # no stored padding, also with a K % 128 tail: the pack is a bijection of
+    # the standard bytes
+    E, N = 2, 32
     kb = K if elem == E4M3 else K // 2
     n = E * N * kb
     codes = np.zeros((E * N, K // 32), np.uint8)
     src = np.zeros(n, np.int64)
     for p, plane in enumerate(_labels(n)):
         wp, _ = oracle.pack_weights(elem, ROW32, E, N, K, plane.reshape(E, N, kb), codes)
+        assert wp.size == n
         src |= wp.astype(np.int64) << (8 * p)
     perm = src                                   # packed[i] = standard[perm[i]]
     assert np.array_equal(np.sort(perm), np.arange(n))
@@ -95,21 +107,26 @@ def test_weight_pack_is_a_permutation(elem):
     np.testing.assert_array_equal(wp[inv], std)
     # lane ownership: lane l = 16 j + r of chunk (t, s) reads row 16 t + r as
     # 16-byte pieces at 16 l (+ 1024): e4m3 K 16 j.. and 64 + 16 j.. of the
-    # step, e2m1 the 32-value block j of the step
-    S, T = K // 128, N // 16
-    for (e, t, s, l) in [(0, 0, 0, 0), (1, 1, 1, 63), (0, 1, 0, 17), (1, 0, 1, 40)]:
+    # step, e2m1 the 32-value block j of the step; a tile is 16 row lengths
+    S, T = -(-K // 128), N // 16
+    chunk, tileb = (2048, 16 * K) if elem == E4M3 else (1024, 8 * K)
+    for (e, t, s, l) in [(0, 0, 0, 0), (1, 1, 1, 63), (0, 1, 0, 17), (1, 0, 1, 40),
+                         (1, 1, S - 1, 5), (0, 0, S - 1, 20)]:
         r, j = l % 16, l // 16
-        base = ((e * T + t) * S + s) * (2048 if elem == E4M3 else 1024)
+        base = (e * T + t) * tileb + s * chunk
         if elem == E4M3:
-            got = np.concatenate([wp[base + 16 * l: base + 16 * l + 16],
-                                  wp[base + 1024 + 16 * l: base + 1024 + 16 * l + 16]])
             row = std.reshape(E, N, K)[e, 16 * t + r]
-            want = np.concatenate([row[128 * s + 16 * j: 128 * s + 16 * j + 16],
-                                   row[128 * s + 64 + 16 * j: 128 * s + 64 + 16 * j + 16]])
+            for h in range(2):
+                k0 = 128 * s + 64 * h + 16 * j
+                if k0 < K:
+                    np.testing.assert_array_equal(
+                        wp[base + 1024 * h + 16 * l: base + 1024 * h + 16 * l + 16],
+                        row[k0: k0 + 16])
         else:
-            got = wp[base + 16 * l: base + 16 * l + 16]
-            want = std.reshape(E, N, K // 2)[e, 16 * t + r, 64 * s + 16 * j: 64 * s + 16 * j + 16]
-        np.testing.assert_array_equal(got, want)
+            b0 = 64 * s + 16 * j
+            if b0 < K // 2:
+                want = std.reshape(E, N, K // 2)[e, 16 * t + r, b0: b0 + 16]
+                np.testing.assert_array_equal(wp[base + 16 * l: base + 16 * l + 16], want)
 
 
 def test_row32_code_pack_is_a_permutation_and_lane_dwords():
@@ -133,13 +150,13 @@ def test_row32_code_pack_is_a_permutation_and_lane_dwords():
                     assert kc[i] == 4 * (4 * q + u) + l // 16
 
 
-def test_padding_bytes_zero_and_codes_128():
+def test_no_weight_padding_and_codes_128():
     E, N, K = 1, 32, 1568
     Kp = 1664
     w = np.full((E, N, K), 0x11, np.uint8)
     codes = np.full((E * N, K // 32), 7, np.uint8)
     wp, cp = oracle.pack_weights(E4M3, ROW32, E, N, K, w, codes)
-    assert wp.size == N * Kp and np.count_nonzero(wp == 0) == N * (Kp - K)
+    assert Kp > K and wp.size == N * K            # the K tail stores no padding
     assert np.count_nonzero(wp == 0x11) == N * K
     S, Q = 13, 4
     assert cp.size == (N // 16) * Q * 256
