@@ -91,13 +91,17 @@ typedef enum { MX_ACT_BF16 = 0, MX_ACT_MXFP8 = 1, MX_ACT_MXFP8_T16 = 2 } mx_act;
 /*
  * Packed weight layout ("W-T16", [weights942] dense_copy / fp4_tile_major
  * tile-major idea; [a16w4] module notes for E2M1).
- *   Kp = K rounded up to a multiple of 128 (zero bytes; padded blocks get code
- *   128, [weights942] dense_copy), S = Kp / 128 steps, T = N / 16 tiles,
- *   Q = ceil(S / 4).  Lane l = 16 j + r.
- *   E4M3: chunk (e, t, s) of 2048 bytes at ((e T + t) S + s) * 2048;
+ *   S = ceil(K / 128) steps, T = N / 16 tiles, Q = ceil(S / 4).  Lane
+ *   l = 16 j + r.  A tile holds exactly 16 row lengths, TILEB = 16 K (E4M3)
+ *   or 8 K (E2M1) bytes: no padding is stored.  When K % 128 != 0 the last
+ *   step's chunk holds only its valid bytes, which are the chunk's first
+ *   512 (E4M3) or 256 (E2M1) bytes per 32-K block present.
+ *   E4M3: chunk (e, t, s) of 2048 bytes at (e T + t) TILEB + 2048 s;
  *         byte 1024 h + 16 l + c = W[e][16 t + r][128 s + 64 h + 16 j + c].
- *   E2M1: chunk (e, t, s) of 1024 bytes at ((e T + t) S + s) * 1024;
+ *   E2M1: chunk (e, t, s) of 1024 bytes at (e T + t) TILEB + 1024 s;
  *         byte 16 l + c = packed byte 64 s + 16 j + c of row 16 t + r.
+ *   Codes are padded to 4 Q steps per row (group) with code 128
+ *   ([weights942] dense_copy pads its steps).
  * Packed codes:
  *   ROW32: 256 bytes per (e, t, q) at ((e T + t) Q + q) * 256;
  *          byte 4 l + u = code[e N + 16 t + r][4 (4 q + u) + j].
