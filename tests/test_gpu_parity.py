@@ -514,3 +514,27 @@ def test_moe_copies_refuses_padding(g):
     with pytest.raises(mx.MXError) as ei:
         g.moe_copies(E2M1, E, Np, inter, K, H, w13, s13, w2, s2)
     assert ei.value.status == 4                   # MX_ERR_VALUE
+
+
+def test_moe_max_pairs(g):
+    """T * topk at the routing scan's maximum (4096 pairs): the ballot walks 64
+    rounds, the slot list is full, and the expert everyone routes to gets 16
+    batches of slots; one pair more is refused before any launch."""
+    import microscaling_quantized_linear_amd as mx
+    E, N, K, T, topk = 16, 32, 128, 512, 8
+    rng = np.random.default_rng(63)
+    w = wl.fp4_bytes(rng, (E, N, K // 2))
+    codes = wl.codes(rng, (E * N, K // 32), 120, 132)
+    x = wl.activations(rng, (T, K))
+    ids, wts = wl.routing(rng, T, E, topk)
+    ids[:, 0] = 3                                # expert 3: every token, 512+ slots
+    sub = ids[:, 1:]
+    sub[sub == 3] = 14                           # a repeated id gives identical rows
+    wp, cp = g.pack(E2M1, ROW32, E, N, K, w, codes)
+    g.assert_close(g.moe(E2M1, E, N, K, wp, cp, x, ids),
+                   oracle.moe_linear(E2M1, E, N, K, w, codes, x, ids), "moe 4096 pairs")
+    g.assert_close(g.moe(E2M1, E, N, K, wp, cp, x, ids, wts),
+                   oracle.moe_linear(E2M1, E, N, K, w, codes, x, ids, wts), "moe 4096 combined")
+    with pytest.raises(mx.MXError) as ei:
+        mx.mx_moe_workspace(E2M1, E, N, K, 4097, 1, 0)
+    assert ei.value.status == 2                  # MX_ERR_SHAPE
