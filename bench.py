@@ -240,7 +240,7 @@ def bench_a16_gemv(torch, mx, g, wl, cid, steps, warmup):
     ms_k = GraphTimer(torch).time(kernel, steps, warmup)
     ms_step = ms_k
     alg = N * K + N * (K // 32)
-    return dict(workload=wl.CONFIGS[cid]["name"], M=M, N=N, K=K, bytes_per_step=alg,
+    return dict(workload=wl.WORKLOADS[cid]["name"], M=M, N=N, K=K, bytes_per_step=alg,
                 weight_copies=nc, ms_per_step=ms_step, ms_kernel=ms_k,
                 value=alg / (ms_step * 1e-3) / 1e9, unit="GB/s",
                 kernel_gbs=alg / (ms_k * 1e-3) / 1e9, kernel="gemv_kernel (A16W8, ROW32)",
@@ -268,7 +268,7 @@ def bench_moe(torch, mx, g, wl, steps, warmup):
     ms_step = ms_k
     touched = len(np.unique(d["ids"]))
     alg = touched * (N * K // 2 + N * (K // 32))
-    return dict(workload=wl.CONFIGS[4]["name"], E=E, N=N, K=K, T=T, topk=topk,
+    return dict(workload=wl.WORKLOADS[4]["name"], E=E, N=N, K=K, T=T, topk=topk,
                 experts_touched=touched, bytes_per_step=alg, weight_copies=nc,
                 ms_per_step=ms_step, ms_kernel=ms_k, value=alg / (ms_step * 1e-3) / 1e9,
                 unit="GB/s", kernel_gbs=alg / (ms_k * 1e-3) / 1e9,
@@ -351,7 +351,7 @@ def bench_gemm(torch, mx, g, wl, steps, warmup):
     ms_step = timer.time(step, steps, warmup)
     ms_k = timer.time(kernel, steps, warmup)
     flop = 2.0 * M * N * K
-    return dict(workload=wl.CONFIGS[5]["name"], M=M, N=N, K=K, flop_per_step=flop,
+    return dict(workload=wl.WORKLOADS[5]["name"], M=M, N=N, K=K, flop_per_step=flop,
                 ms_per_step=ms_step, ms_kernel=ms_k, value=flop / (ms_step * 1e-3) / 1e12,
                 unit="TFLOP/s", kernel_tflops=flop / (ms_k * 1e-3) / 1e12,
                 kernel="gemm_w8a8_kernel (BLK32, T16 activations)",
@@ -380,7 +380,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is "
-              "a single-GPU kernel library and this build measures no multi-GPU path.",
+              "a single-GPU kernel library and measures no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
     import torch

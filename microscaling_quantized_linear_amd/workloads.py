@@ -5,8 +5,8 @@ and imports neither the HIP library nor the oracle.  Tests, the benchmark and
 the smoke check all take their inputs from here, so the oracle and the GPU see
 identical bytes.
 
-Every tensor comes from numpy's PCG64 seeded with ``[seed, config_id,
-tensor_id]``.  Distributions:
+Every tensor comes from numpy's PCG64 seeded with ``[seed, wid,
+tensor_id]`` (wid: the workload's id below).  Distributions:
 
 * e4m3 weight bytes: uniform over the 254 non-NaN codes (0x7F and 0xFF left out).
 * e2m1 weight bytes: uniform bytes, i.e. uniform nibbles, -0 (0x8) included.
@@ -21,7 +21,7 @@ from __future__ import annotations
 
 import numpy as np
 
-# tensor ids inside one config's seed stream
+# tensor ids inside one workload's seed stream
 T_WEIGHT, T_CODES, T_X, T_OUTLIER, T_ROUTE, T_BIAS = range(6)
 
 E4M3, E2M1 = 0, 1
@@ -29,8 +29,8 @@ ROW32, BLK32 = 0, 1
 RULE_OCP, RULE_CEIL448 = 0, 1
 ACT_BF16, ACT_MXFP8 = 0, 1
 
-# The five workloads.  "name" is what the benchmark prints as config.workload.
-CONFIGS = {
+# The five workloads, by id.  "name" is what the benchmark prints as config.workload.
+WORKLOADS = {
     1: dict(name="mxfp8_a16w8_gemv_M1_N256_K512_row32", kind="linear", elem=E4M3,
             layout=ROW32, act=ACT_BF16, Ms=(1,), N=256, K=512, codes=(120, 134),
             outliers=0.0),
@@ -49,8 +49,8 @@ CONFIGS = {
 }
 
 
-def rng(config_id: int, tensor_id: int, seed: int = 0) -> np.random.Generator:
-    return np.random.default_rng([seed, config_id, tensor_id])
+def rng(wid: int, tensor_id: int, seed: int = 0) -> np.random.Generator:
+    return np.random.default_rng([seed, wid, tensor_id])
 
 
 def e4m3_bytes(g: np.random.Generator, shape) -> np.ndarray:
@@ -100,41 +100,41 @@ def routing(g: np.random.Generator, T: int, E: int, topk: int):
     return ids, w
 
 
-def linear_inputs(config_id: int, M=None, N=None, K=None, seed: int = 0):
+def linear_inputs(wid: int, M=None, N=None, K=None, seed: int = 0):
     """Inputs of a dense config (optionally at another shape, same recipe).
 
     Returns dict(w [N, K] uint8, codes ROW32 [N, K/32] or BLK32 [N/32, K/32],
     x bf16 bits [M, K]); M defaults to the largest M of the config.
     """
-    c = CONFIGS[config_id]
+    c = WORKLOADS[wid]
     N = c["N"] if N is None else N
     K = c["K"] if K is None else K
     M = max(c["Ms"]) if M is None else M
-    w = e4m3_bytes(rng(config_id, T_WEIGHT, seed), (N, K))
+    w = e4m3_bytes(rng(wid, T_WEIGHT, seed), (N, K))
     cshape = (N, K // 32) if c["layout"] == ROW32 else (N // 32, K // 32)
-    cd = codes(rng(config_id, T_CODES, seed), cshape, *c["codes"])
-    x = activations(rng(config_id, T_X, seed), (M, K), c["outliers"],
-                    rng(config_id, T_OUTLIER, seed))
+    cd = codes(rng(wid, T_CODES, seed), cshape, *c["codes"])
+    x = activations(rng(wid, T_X, seed), (M, K), c["outliers"],
+                    rng(wid, T_OUTLIER, seed))
     return dict(w=w, codes=cd, x=x, M=M, N=N, K=K, elem=c["elem"],
                 layout=c["layout"], act=c["act"], rule=c.get("rule", RULE_OCP))
 
 
-def moe_inputs(config_id: int = 4, E=None, N=None, K=None, T=None, topk=None,
+def moe_inputs(wid: int = 4, E=None, N=None, K=None, T=None, topk=None,
                seed: int = 0):
     """Inputs of the MoE config: w [E, N, K/2] e2m1, codes [E*N, K/32], x, ids, weights."""
-    c = CONFIGS[config_id]
+    c = WORKLOADS[wid]
     E = c["E"] if E is None else E
     N = c["N"] if N is None else N
     K = c["K"] if K is None else K
     T = c["T"] if T is None else T
     topk = c["topk"] if topk is None else topk
-    w = fp4_bytes(rng(config_id, T_WEIGHT, seed), (E, N, K // 2))
-    cd = codes(rng(config_id, T_CODES, seed), (E * N, K // 32), *c["codes"])
-    x = activations(rng(config_id, T_X, seed), (T, K))
-    ids, wts = routing(rng(config_id, T_ROUTE, seed), T, E, topk)
+    w = fp4_bytes(rng(wid, T_WEIGHT, seed), (E, N, K // 2))
+    cd = codes(rng(wid, T_CODES, seed), (E * N, K // 32), *c["codes"])
+    x = activations(rng(wid, T_X, seed), (T, K))
+    ids, wts = routing(rng(wid, T_ROUTE, seed), T, E, topk)
     return dict(w=w, codes=cd, x=x, ids=ids, weights=wts, E=E, N=N, K=K, T=T,
                 topk=topk, elem=E2M1, layout=ROW32)
 
 
-def bias(config_id: int, N: int, seed: int = 0) -> np.ndarray:
-    return activations(rng(config_id, T_BIAS, seed), (N,))
+def bias(wid: int, N: int, seed: int = 0) -> np.ndarray:
+    return activations(rng(wid, T_BIAS, seed), (N,))

@@ -3,7 +3,7 @@
 Packs and quantized activations must match bit for bit; bf16 outputs must
 meet the bar in tests/mxgpu.py (relative L2 <= 2e-3, every element within
 1e-2 of its oracle row's largest magnitude).  Small cases span several tiles
-and ragged K tails; the five workload configurations run at full size, with
+and ragged K tails; the five workloads run at full size, with
 the 4096-token GEMM checked on sampled outputs."""
 import numpy as np
 import pytest
@@ -49,7 +49,7 @@ def test_pack_bit_exact_small(g, elem, layout, E, N, K):
 
 
 @pytest.mark.parametrize("cid", [1, 2, 3, 5])
-def test_pack_bit_exact_configs(g, cid):
+def test_pack_bit_exact_workloads(g, cid):
     d = wl.linear_inputs(cid, M=1)
     wp, cp = g.pack(d["elem"], d["layout"], 1, d["N"], d["K"], d["w"], d["codes"])
     owp, ocp = oracle.pack_weights(d["elem"], d["layout"], 1, d["N"], d["K"], d["w"], d["codes"])
@@ -57,7 +57,7 @@ def test_pack_bit_exact_configs(g, cid):
     assert np.array_equal(cp.cpu().numpy(), ocp)
 
 
-def test_pack_bit_exact_moe_config(g):
+def test_pack_bit_exact_moe_workload(g):
     d = wl.moe_inputs(4)
     wp, cp = g.pack(E2M1, ROW32, d["E"], d["N"], d["K"], d["w"], d["codes"])
     owp, ocp = oracle.pack_weights(E2M1, ROW32, d["E"], d["N"], d["K"], d["w"], d["codes"])
@@ -196,18 +196,18 @@ def test_extreme_codes_a16(g):
     g.assert_close(y, ref, "extreme codes a16")
 
 
-# ------------------------------------------------------------------ configs
+# ------------------------------------------------------------------ the five workloads
 
-def test_config1_full(g):
+def test_a16w8_gemv_m1_n256_k512_full(g):
     d = wl.linear_inputs(1)
     wp, cp = g.pack(E4M3, ROW32, 1, d["N"], d["K"], d["w"], d["codes"])
     ref = oracle.linear(E4M3, ROW32, d["N"], d["K"], d["w"], d["codes"], d["M"], BF16, x=d["x"])
     y = g.linear(E4M3, ROW32, d["N"], d["K"], wp, cp, BF16, x=d["x"])
-    g.assert_close(y, ref, "config 1")
+    g.assert_close(y, ref, "a16w8 M=1 N=256 K=512")
 
 
 @pytest.mark.parametrize("rule", [OCP, CEIL])
-def test_config2_full(g, rule):
+def test_w8a8_gemv_n7168_k7168_full(g, rule):
     d = wl.linear_inputs(2)
     N, K = d["N"], d["K"]
     wp, cp = g.pack(E4M3, BLK32, 1, N, K, d["w"], d["codes"])
@@ -218,18 +218,18 @@ def test_config2_full(g, rule):
         assert np.array_equal(xq, oq) and np.array_equal(xc, oc)
         ref = oracle.linear(E4M3, BLK32, N, K, d["w"], d["codes"], M, MXFP8, xq=oq, xcodes=oc)
         y = g.linear(E4M3, BLK32, N, K, wp, cp, MXFP8, x=x, rule=rule)
-        g.assert_close(y, ref, f"config 2 M={M}")
+        g.assert_close(y, ref, f"w8a8 N=K=7168 M={M}")
         y2 = g.linear(E4M3, BLK32, N, K, wp, cp, MXFP8, x=x, rule=rule)
         assert np.array_equal(y, y2), "not deterministic"
 
 
-def test_config3_full_and_negative_zero(g):
+def test_a16w8_gemv_m8_n4096_k1568_full_and_negative_zero(g):
     d = wl.linear_inputs(3)
     N, K, M = d["N"], d["K"], d["M"]
     wp, cp = g.pack(E4M3, ROW32, 1, N, K, d["w"], d["codes"])
     ref = oracle.linear(E4M3, ROW32, N, K, d["w"], d["codes"], M, BF16, x=d["x"])
     y = g.linear(E4M3, ROW32, N, K, wp, cp, BF16, x=d["x"])
-    g.assert_close(y, ref, "config 3")
+    g.assert_close(y, ref, "a16w8 M=8 N=4096 K=1568")
     # -0 (0x80) decodes equal to +0: swapping them leaves the output unchanged
     w0 = d["w"].copy()
     w0[w0 == 0x80] = 0x00
@@ -244,22 +244,22 @@ def test_config3_full_and_negative_zero(g):
     oq, oc = oracle.quant_act(d["x"], OCP)
     ref8 = oracle.linear(E4M3, ROW32, N, K, d["w"], d["codes"], M, MXFP8, xq=oq, xcodes=oc)
     y8 = g.linear(E4M3, ROW32, N, K, wp, cp, MXFP8, x=d["x"], rule=OCP)
-    g.assert_close(y8, ref8, "config 3 W8A8")
+    g.assert_close(y8, ref8, "w8a8 M=8 N=4096 K=1568")
 
 
-def test_config4_moe_full(g):
+def test_moe_e32_n3072_k3072_t16_top8_full(g):
     d = wl.moe_inputs(4)
     E, N, K = d["E"], d["N"], d["K"]
     wp, cp = g.pack(E2M1, ROW32, E, N, K, d["w"], d["codes"])
     ref = oracle.moe_linear(E2M1, E, N, K, d["w"], d["codes"], d["x"], d["ids"])
     y = g.moe(E2M1, E, N, K, wp, cp, d["x"], d["ids"])
-    g.assert_close(y, ref, "config 4 per slot")
+    g.assert_close(y, ref, "moe E=32 per slot")
     refc = oracle.moe_linear(E2M1, E, N, K, d["w"], d["codes"], d["x"], d["ids"], d["weights"])
     yc = g.moe(E2M1, E, N, K, wp, cp, d["x"], d["ids"], d["weights"])
-    g.assert_close(yc, refc, "config 4 combined")
+    g.assert_close(yc, refc, "moe E=32 combined")
 
 
-def test_config5_gemm_sampled(g):
+def test_gemm_m4096_n7168_k7168_sampled(g):
     d = wl.linear_inputs(5)
     N, K, M = d["N"], d["K"], d["M"]
     wp, cp = g.pack(E4M3, BLK32, 1, N, K, d["w"], d["codes"])
@@ -272,7 +272,7 @@ def test_config5_gemm_sampled(g):
     assert np.array_equal(gq, oq) and np.array_equal(gc, oc)
     # full output rows for the sampled tokens
     ref = oracle.linear(E4M3, BLK32, N, K, d["w"], d["codes"], len(rows), MXFP8, xq=oq, xcodes=oc)
-    g.assert_close(y[rows], ref, "config 5 rows")
+    g.assert_close(y[rows], ref, "gemm M=4096 rows")
 
 
 # ------------------------------------------------------------------ MoE edges
