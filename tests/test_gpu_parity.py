@@ -393,6 +393,8 @@ MOE_SHAPES = [
     (E4M3, 5, 32, 3072, 16, 4),
     (E2M1, 64, 16, 1024, 16, 8),      # one tile per expert, many experts per workgroup
     (E2M1, 300, 16, 1024, 4, 4),
+    (E2M1, 16, 64, 512, 5, 12),       # combine over more than 8 slots (two groups)
+    (E2M1, 24, 32, 256, 3, 24),       # topk = E, three groups of 8
 ]
 
 
