@@ -540,3 +540,41 @@ def test_moe_max_pairs(g):
     with pytest.raises(mx.MXError) as ei:
         mx.mx_moe_workspace(E2M1, E, N, K, 4097, 1, 0)
     assert ei.value.status == 2                  # MX_ERR_SHAPE
+
+
+@pytest.mark.parametrize("path", ["a16", "w8a8_fused", "w8a8_gemm", "w8a8_t16"])
+def test_strided_activation_and_output(g, path):
+    """Leading dimensions above K (activations) and N (output): every path
+    gives the contiguous call's bits and leaves the padding columns of y
+    untouched."""
+    import torch
+    import microscaling_quantized_linear_amd as mx
+    layout = BLK32 if path != "a16" else ROW32
+    M = {"a16": 5, "w8a8_fused": 16, "w8a8_gemm": 200, "w8a8_t16": 7}[path]
+    N, K = 512, 1024
+    w, codes, x, bias = _dense_inputs([48, M, N, K, layout], E4M3, layout, M, N, K)
+    wp, cp = g.pack(E4M3, layout, 1, N, K, w, codes)
+    act = BF16 if path == "a16" else MXFP8
+    want = g.linear(E4M3, layout, N, K, wp, cp, act, x=x, rule=OCP, bias=bias)
+    ldx, ldy = K + 24, N + 40
+    xs = np.zeros((M, ldx), np.uint16)
+    xs[:, :K] = x
+    xd = g.dev(xs)
+    bd = g.dev(bias)
+    y = torch.full((M, ldy), 0x7A7A, dtype=torch.int16, device=g.DEV)
+    if path == "w8a8_t16":
+        qb, cb = mx.mx_act_t16_sizes(M, K)
+        xq = torch.empty(qb, dtype=torch.uint8, device=g.DEV)
+        xc = torch.empty(cb, dtype=torch.uint8, device=g.DEV)
+        mx.mx_quant_act_t16(M, K, xd, ldx, xq, xc, OCP)
+        mx.mx_linear(E4M3, layout, N, K, wp, cp, M, MXFP8_T16, 0, None, 0, xq, 0, xc, 0, bd, y,
+                     ldy, None, 0)
+    else:
+        need = mx.mx_linear_workspace(E4M3, layout, N, K, M, act, 0)
+        ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=g.DEV)
+        mx.mx_linear(E4M3, layout, N, K, wp, cp, M, act, OCP, xd, ldx, None, 0, None, 0, bd, y,
+                     ldy, ws, need)
+    torch.cuda.synchronize()
+    got = g.host_u16(y)
+    np.testing.assert_array_equal(got[:, :N], want)
+    assert (got[:, N:] == 0x7A7A).all()
