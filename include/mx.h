@@ -217,7 +217,8 @@ mx_status mx_quant_act_t16(int64_t M, int64_t K, const void *x, int64_t ldx, voi
  *     T16 activation, round256(MB * S * 2048) + MB * Q * 256;
  *   act == MX_ACT_MXFP8 pre-quantized row-major with M > 64 (prefill GEMM):
  *     the same size: the GEMM reads the T16 layout, so the bytes and codes
- *     are restaged into it;
+ *     are restaged into it (0 in the batch-invariant mode, where the GEMV
+ *     reads them as given: see mx_set_batch_invariant);
  *   otherwise 0 (MX_ACT_BF16, MX_ACT_MXFP8_T16, or pre-quantized M <= 64).
  * (K > 8192 with M <= 64 quantized inside the call is the exception: the
  * row-major staging round256(M * Kp) + round256(M * Kp / 32).)
