@@ -85,25 +85,21 @@ mx_status shape_ok(int elem, int layout, int64_t E, int64_t N, int64_t K) {
     return MX_OK;
 }
 
-// -1 unknown, 0 unsupported, 1 gfx950; one entry per device ordinal
+// one entry per device ordinal: 0 not yet known (the zero-initialized
+// state, valid before any constructor runs), 1 not gfx950, 2 gfx950
 std::atomic<int> g_arch[64];
-struct ArchInit {
-    ArchInit() {
-        for (auto &a : g_arch) a.store(-1);
-    }
-} g_arch_init;
 
 mx_status device_ok() {
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MX_ERR_DEVICE;
     if (dev < 64) {
-        int v = g_arch[dev].load();
-        if (v >= 0) return v ? MX_OK : MX_ERR_DEVICE;
+        const int v = g_arch[dev].load();
+        if (v != 0) return v == 2 ? MX_OK : MX_ERR_DEVICE;
     }
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MX_ERR_DEVICE;
     const int ok = mx_arch_supported(prop.gcnArchName);
-    if (dev < 64) g_arch[dev].store(ok);
+    if (dev < 64) g_arch[dev].store(ok ? 2 : 1);
     return ok ? MX_OK : MX_ERR_DEVICE;
 }
 
