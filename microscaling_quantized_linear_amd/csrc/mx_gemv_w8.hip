@@ -524,6 +524,143 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
     *reinterpret_cast<v2u *>(p.y + row * p.ldy + n0) = o;
 }
 
+// The even-shape GEMV on a pre-quantized row-major activation: mx_quant_act's
+// e4m3 [M, ldq] with row-major codes [M, ldc], the form [rocm_native]
+// apply_weights takes as a quantized activation.  Loads of 8 tokens x 128
+// contiguous bytes (one step of each) instead of the LDS copies of 16 rows x
+// 64 bytes, which the rows' stride concentrates on few L2 channels; a padded
+// 16 x 144-byte LDS tile per wavefront turns them into the operand order
+// (rows 144 bytes apart: the 16-byte reads of the 16 tokens fall on distinct
+// banks).  Lane (r, j)'s scale byte is the code of token 16 mb + r, block
+// 4 s + j, read as a byte from the row-major codes.  Weight chunks as in the
+// T16 kernel: the first step's first, all of them in flight.  The product is
+// the T16 path's, bit for bit (same bytes, codes and MFMA order).
+template <int LAYOUT, int G, int SPW, int NW>
+__global__ void __launch_bounds__(NW * 64) gemv_w8_rm_kernel(GemvW8Args p) {
+    constexpr int XROW = 144;                          // padded LDS row of one token
+    __shared__ v4f red[NW][G][64];
+    __shared__ __attribute__((aligned(16))) uint8_t xt[NW][16 * XROW];
+
+    const int lane = threadIdx.x % 64;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const int r = lane % 16, j = lane / 16;
+    const uint32_t S = (uint32_t)(p.K / 128), Q = (S + 3) / 4;
+    const uint32_t mb = blockIdx.y;
+    const uint32_t t0 = blockIdx.x * G;
+    const uint32_t s0 = wave * SPW;
+    const uint32_t lo = 16 * lane;
+
+    // ---- 1. the first step's weight chunks ----
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w + (size_t)t0 * S * 2048, G * S * 2048);
+    v4u wv[SPW][G][2];
+    auto wload = [&](int i) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                wv[i][g][h] = __builtin_amdgcn_raw_buffer_load_b128(
+                    wr, lo, (int)((g * S + s0 + i) * 2048 + h * 1024), kNT);
+    };
+    wload(0);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 2. activation bytes of the wavefront's steps (load u of a step:
+    // token 16 mb + 8 u + l / 8, bytes 16 (l % 8) of its 128; tokens past M
+    // read zeros through the resource bounds), then the codes ----
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.xq, (uint32_t)(p.M * p.ldq));
+    uint32_t xo[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int64_t tok = 16 * (int64_t)mb + 8 * u + lane / 8;
+        xo[u] = tok < p.M ? (uint32_t)(tok * p.ldq) + 16 * (lane % 8) : kOOB;
+    }
+    v4u xv[SPW][2];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i)
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            xv[i][u] = __builtin_amdgcn_raw_buffer_load_b128(xr, xo[u], (int)(128 * (s0 + i)), 0);
+    const __amdgpu_buffer_rsrc_t xcr = make_rsrc(p.xc, (uint32_t)(p.M * p.ldc));
+    const int64_t tr = 16 * (int64_t)mb + r;
+    const uint32_t cxo = tr < p.M ? (uint32_t)(tr * p.ldc) + (uint32_t)j : kOOB;
+    uint32_t cx[SPW];
+#pragma unroll
+    for (int i = 0; i < SPW; ++i)
+        cx[i] = __builtin_amdgcn_raw_buffer_load_b8(xcr, cxo, (int)(4 * (s0 + i)), 0);
+    uint32_t cws[SPW][G];
+    if constexpr (LAYOUT == BLK32) {
+        const __amdgpu_buffer_rsrc_t cr = make_rsrc(p.codes, (uint32_t)(p.N / 32) * Q * 16);
+#pragma unroll
+        for (int i = 0; i < SPW; ++i)
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                if (G % 2 == 0 && g % 2 == 1) {
+                    cws[i][g] = cws[i][g - 1];
+                    continue;
+                }
+                const uint32_t s = s0 + i;
+                cws[i][g] = __builtin_amdgcn_raw_buffer_load_b8(
+                    cr, 4 * j, (int)((((t0 + g) / 2) * Q + s / 4) * 16 + s % 4), 0);
+            }
+    } else {
+        const __amdgpu_buffer_rsrc_t cr = make_rsrc(p.codes, (uint32_t)(p.N / 16) * Q * 256);
+#pragma unroll
+        for (int i = 0; i < SPW; ++i)
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const uint32_t s = s0 + i;
+                cws[i][g] = __builtin_amdgcn_raw_buffer_load_b8(
+                    cr, 4 * lane, (int)(((t0 + g) * Q + s / 4) * 256 + s % 4), 0);
+            }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 3. the remaining weight chunks ----
+#pragma unroll
+    for (int i = 1; i < SPW; ++i) wload(i);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 4. per step: LDS transpose, one scaled MFMA per tile ----
+    uint8_t *tile = xt[wave];
+    v4f acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
+    static_for<0, SPW>([&](auto iconst) {
+        constexpr int i = decltype(iconst)::value;
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            *reinterpret_cast<v4u *>(tile + (8 * u + lane / 8) * XROW + 16 * (lane % 8)) =
+                xv[i][u];
+        // lane (r, j): token r, K 16 j .. 16 j + 15 and 64 + 16 j .. of the step
+        const uint8_t *mine = tile + r * XROW + 16 * j;
+        const v8i bq = cat8(*reinterpret_cast<const v4u *>(mine),
+                            *reinterpret_cast<const v4u *>(mine + 64));
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            acc[g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                cat8(wv[i][g][0], wv[i][g][1]), bq, acc[g], 0, 0, 0, (int)cws[i][g], 0,
+                (int)cx[i]);
+        __builtin_amdgcn_sched_barrier(0);
+    });
+
+    // ---- 5. wavefront-order reduction; wavefront g finishes tile g ----
+#pragma unroll
+    for (int g = 0; g < G; ++g) red[wave][g][lane] = acc[g];
+    __syncthreads();
+    const int64_t row = 16 * (int64_t)mb + r;
+    if (wave >= G || row >= p.M) return;
+    const int g = wave;
+    v4f a = red[0][g][lane];
+#pragma unroll
+    for (int w2 = 1; w2 < NW; ++w2) a += red[w2][g][lane];
+    const int64_t n0 = 16 * (int64_t)(t0 + g) + 4 * j;
+    float v[4] = {a[0], a[1], a[2], a[3]};
+    if (p.bias)
+        for (int e = 0; e < 4; ++e) v[e] += bf16_to_f32(p.bias[n0 + e]);
+    v2u o = {bf16_bits(v[0]) | (bf16_bits(v[1]) << 16), bf16_bits(v[2]) | (bf16_bits(v[3]) << 16)};
+    *reinterpret_cast<v2u *>(p.y + row * p.ldy + n0) = o;
+}
+
 // launch helpers of the even-shape kernels: SPW in {1, 2, 4, 7, 8}, G in
 // {1, 2, 4} with G * SPW <= 16, eight wavefronts
 template <int G, class F>
@@ -626,6 +763,19 @@ hipError_t launch_gemv_w8(int layout, bool xfrag, const GemvW8Args &a, const Gem
                 hipLaunchKernelGGL((gemv_w8_even_kernel<ROW32, G, SPW, 8>), grid, block, 0, st, a);
             else
                 hipLaunchKernelGGL((gemv_w8_even_kernel<BLK32, G, SPW, 8>), grid, block, 0, st, a);
+            return hipSuccess;
+        });
+        if (e != hipSuccess) return e;
+        return hipGetLastError();
+    }
+    if (!xfrag && gemv_w8_even(a.N, a.K, pl)) {
+        const dim3 grid((unsigned)(a.N / 16 / pl.g), (unsigned)((a.M + 15) / 16)), block(512);
+        const hipError_t e = even_dispatch(pl, [&](auto gc, auto sc) -> hipError_t {
+            constexpr int G = decltype(gc)::value, SPW = decltype(sc)::value;
+            if (layout == ROW32)
+                hipLaunchKernelGGL((gemv_w8_rm_kernel<ROW32, G, SPW, 8>), grid, block, 0, st, a);
+            else
+                hipLaunchKernelGGL((gemv_w8_rm_kernel<BLK32, G, SPW, 8>), grid, block, 0, st, a);
             return hipSuccess;
         });
         if (e != hipSuccess) return e;
