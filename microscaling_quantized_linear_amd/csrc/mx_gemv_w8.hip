@@ -526,20 +526,23 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
 
 // The even-shape GEMV on a pre-quantized row-major activation: mx_quant_act's
 // e4m3 [M, ldq] with row-major codes [M, ldc], the form [rocm_native]
-// apply_weights takes as a quantized activation.  Loads of 8 tokens x 128
-// contiguous bytes (one step of each) instead of the LDS copies of 16 rows x
-// 64 bytes, which the rows' stride concentrates on few L2 channels; a padded
-// 16 x 144-byte LDS tile per wavefront turns them into the operand order
-// (rows 144 bytes apart: the 16-byte reads of the 16 tokens fall on distinct
-// banks).  Lane (r, j)'s scale byte is the code of token 16 mb + r, block
-// 4 s + j, read as a byte from the row-major codes.  Weight chunks as in the
-// T16 kernel: the first step's first, all of them in flight.  The product is
-// the T16 path's, bit for bit (same bytes, codes and MFMA order).
+// apply_weights takes as a quantized activation.  The activation bytes go
+// straight into LDS (buffer loads with an LDS destination, as in the T16
+// kernel), but each 1 KB copy reads 8 tokens x 128 contiguous bytes (one step
+// of each): copy u of step i, lane l = 8 t + q fetches token r = 8 u + t's
+// 16-byte piece q ^ (r / 2) into LDS slot (t, q).  Rows of 16 tokens x 64
+// bytes per copy instead, with the caller's row stride, concentrate each copy
+// on few L2 channels.  Lane (r, j) then reads its pieces j and 4 + j (K 16 j
+// .. and 64 + 16 j .. of the step) at slot (r % 8, p ^ (r / 2)) of copy r / 8:
+// the 16 tokens' reads fall on 16 distinct 16-byte bank groups.  Its scale
+// byte is token r's code of block 4 s + j, read from the row-major codes.
+// Weight chunks as in the T16 kernel.  The product is the T16 path's, bit for
+// bit (same bytes, codes and MFMA order).
 template <int LAYOUT, int G, int SPW, int NW>
 __global__ void __launch_bounds__(NW * 64) gemv_w8_rm_kernel(GemvW8Args p) {
-    constexpr int XROW = 144;                          // padded LDS row of one token
+    static_assert(2 * G * (SPW - 1) < 64, "vmcnt holds 6 bits");
+    __shared__ __attribute__((aligned(1024))) uint8_t xs[NW][SPW * 2048];
     __shared__ v4f red[NW][G][64];
-    __shared__ __attribute__((aligned(16))) uint8_t xt[NW][16 * XROW];
 
     const int lane = threadIdx.x % 64;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
@@ -564,22 +567,28 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_rm_kernel(GemvW8Args p) {
     wload(0);
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- 2. activation bytes of the wavefront's steps (load u of a step:
-    // token 16 mb + 8 u + l / 8, bytes 16 (l % 8) of its 128; tokens past M
-    // read zeros through the resource bounds), then the codes ----
+    // ---- 2. activation bytes of the wavefront's steps -> its LDS (tokens
+    // past M read zeros through the resource bounds) ----
+    uint8_t *myx = xs[wave];
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(p.xq, (uint32_t)(p.M * p.ldq));
     uint32_t xo[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        const int64_t tok = 16 * (int64_t)mb + 8 * u + lane / 8;
-        xo[u] = tok < p.M ? (uint32_t)(tok * p.ldq) + 16 * (lane % 8) : kOOB;
+        const int tr = 8 * u + lane / 8;                 // token within the tile
+        const int64_t tok = 16 * (int64_t)mb + tr;
+        const uint32_t piece = (uint32_t)((lane % 8) ^ (tr / 2));
+        xo[u] = tok < p.M ? (uint32_t)(tok * p.ldq) + 16 * piece : kOOB;
     }
-    v4u xv[SPW][2];
 #pragma unroll
     for (int i = 0; i < SPW; ++i)
 #pragma unroll
         for (int u = 0; u < 2; ++u)
-            xv[i][u] = __builtin_amdgcn_raw_buffer_load_b128(xr, xo[u], (int)(128 * (s0 + i)), 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                xr, (lds_void_w8 *)(myx + (2 * i + u) * 1024), 16, (int)xo[u],
+                (int)(128 * (s0 + i)), 0, 0);
+
+    // ---- 3. codes: the activation's from the row-major codes, the weights'
+    // one byte per step (byte u of a code dword is step 4 q + u) ----
     const __amdgpu_buffer_rsrc_t xcr = make_rsrc(p.xc, (uint32_t)(p.M * p.ldc));
     const int64_t tr = 16 * (int64_t)mb + r;
     const uint32_t cxo = tr < p.M ? (uint32_t)(tr * p.ldc) + (uint32_t)j : kOOB;
@@ -615,35 +624,37 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_rm_kernel(GemvW8Args p) {
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- 3. the remaining weight chunks ----
+    // ---- 4. the remaining weight chunks ----
 #pragma unroll
     for (int i = 1; i < SPW; ++i) wload(i);
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- 4. per step: LDS transpose, one scaled MFMA per tile ----
-    uint8_t *tile = xt[wave];
+    // Everything before the remaining weight chunks has landed once at most
+    // that many loads are outstanding (in-order completion); the compiler
+    // does not count the copies into LDS, hence the explicit wait.
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * G * (SPW - 1)));
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- 5. one scaled MFMA per tile and step ----
+    const uint8_t *rd0 = myx + (r / 8) * 1024 + (r % 8) * 128;
+    const uint32_t sw = (uint32_t)(r / 2);
+    const uint32_t pa = 16u * ((uint32_t)j ^ sw), pb = 16u * ((uint32_t)(4 + j) ^ sw);
     v4f acc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
     static_for<0, SPW>([&](auto iconst) {
         constexpr int i = decltype(iconst)::value;
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            *reinterpret_cast<v4u *>(tile + (8 * u + lane / 8) * XROW + 16 * (lane % 8)) =
-                xv[i][u];
-        // lane (r, j): token r, K 16 j .. 16 j + 15 and 64 + 16 j .. of the step
-        const uint8_t *mine = tile + r * XROW + 16 * j;
-        const v8i bq = cat8(*reinterpret_cast<const v4u *>(mine),
-                            *reinterpret_cast<const v4u *>(mine + 64));
+        const uint8_t *base = rd0 + i * 2048;
+        const v8i bq = cat8(*reinterpret_cast<const v4u *>(base + pa),
+                            *reinterpret_cast<const v4u *>(base + pb));
 #pragma unroll
         for (int g = 0; g < G; ++g)
             acc[g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 cat8(wv[i][g][0], wv[i][g][1]), bq, acc[g], 0, 0, 0, (int)cws[i][g], 0,
                 (int)cx[i]);
-        __builtin_amdgcn_sched_barrier(0);
     });
 
-    // ---- 5. wavefront-order reduction; wavefront g finishes tile g ----
+    // ---- 6. wavefront-order reduction; wavefront g finishes tile g ----
 #pragma unroll
     for (int g = 0; g < G; ++g) red[wave][g][lane] = acc[g];
     __syncthreads();
