@@ -284,3 +284,21 @@ def test_binding_raises_without_touching_the_device():
     with pytest.raises(mx.MXError) as ei:
         mx.mx_packed_sizes(0, 0, 1, 24, 512)
     assert ei.value.status == SHAPE
+
+
+def test_fused_quant_kill_switch():
+    """MX_FUSED_QUANT=0 (read once per process) turns off the quantization
+    inside the decode GEMV: the same call then stages the T16 activation in
+    the workspace (a quantization launch before the GEMV, whose output the
+    GPU tests hold equal to the fused one bit for bit)."""
+    import subprocess
+    import sys
+    args = (0, 1, 7168, 7168, 16, 1, False)         # W8A8 BLK32, M=16, bf16 input
+    assert mx.mx_linear_workspace(*args) == 0
+    code = ("import microscaling_quantized_linear_amd as mx; "
+            f"print(mx.mx_linear_workspace(*{args!r}))")
+    env = dict(os.environ, MX_FUSED_QUANT="0")
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                         text=True, timeout=120, check=True).stdout
+    t16 = 16 * 7168 + 16 * (7168 // 32)                # one 16-token tile of bytes and codes
+    assert int(out.strip().splitlines()[-1]) >= t16
