@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
     ap.add_argument("--only", default=None,
                     help="run one workload only (gemv16, gemv1, gemv4, gemv16r, a16_c1, a16_c3, "
-                         "moe, moe_block, gemm)")
+                         "moe, moe_block, gemm, gemv16_ceil, gemm_ceil)")
     ap.add_argument("--eager", action="store_true",
                     help="launch without HIP graphs (for hardware-counter runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -161,13 +161,16 @@ def setup_dense(torch, mx, g, wl, cid, M, rotate=True):
     return d, wps, cps
 
 
-def bench_w8a8_gemv(torch, mx, g, wl, M, steps, warmup, rowmajor=False):
+def bench_w8a8_gemv(torch, mx, g, wl, M, steps, warmup, rowmajor=False, rule=None):
     """W8A8 decode GEMV, N = K = 7168, 32x32 block codes.
 
     Default: one mx_linear call per step with the activation quantized inside
     the call (per token, OCP rule, into the T16 layout), then the GEMV; the
     kernel-only timing runs the same GEMV on a pre-quantized T16 activation.
-    rowmajor: mx_quant_act (row-major output) then mx_linear on it."""
+    rowmajor: mx_quant_act (row-major output) then mx_linear on it.
+    rule: the activation scale rule (default OCP; MX_RULE_CEIL448 is the
+    pages' ceil(log2(amax / 448)) rule, reported as its own line)."""
+    rule = mx.MX_RULE_OCP if rule is None else rule
     d, wps, cps = setup_dense(torch, mx, g, wl, 2, M)
     N, K = d["N"], d["K"]
     x = g.dev(d["x"][:M])
@@ -197,7 +200,7 @@ def bench_w8a8_gemv(torch, mx, g, wl, M, steps, warmup, rowmajor=False):
         mx.mx_quant_act_t16(M, K, x, K, xq, xc, mx.MX_RULE_OCP)
 
         def step(i):
-            mx.mx_linear(E, L, N, K, wps[i % nc], cps[i % nc], M, A8, mx.MX_RULE_OCP, x, K,
+            mx.mx_linear(E, L, N, K, wps[i % nc], cps[i % nc], M, A8, rule, x, K,
                          None, 0, None, 0, None, y, N, ws, need)
 
         def kernel(i):
@@ -211,12 +214,14 @@ def bench_w8a8_gemv(torch, mx, g, wl, M, steps, warmup, rowmajor=False):
         # with the quantization inside the GEMV the step is one launch of
         # gemv_w8_fused_kernel: the step's time is that kernel's time
         ms_k = ms_step if fused else ms_t16
-        how = ("mx_linear with MXFP8 quantization (OCP rule) inside the GEMV: one launch"
-               if fused else "mx_linear with in-call MXFP8 quantization (OCP rule) then the GEMV")
+        rname = "OCP rule" if rule == mx.MX_RULE_OCP else "ceil(log2(amax/448)) rule"
+        how = (f"mx_linear with MXFP8 quantization ({rname}) inside the GEMV: one launch"
+               if fused else f"mx_linear with in-call MXFP8 quantization ({rname}) then the GEMV")
         kname = ("gemv_w8_fused_kernel (BLK32, per-token quantization inside)" if fused
                  else "gemv_w8_even_kernel (BLK32, T16 activations)")
     alg = N * K + (N // 32) * (K // 32)
-    out = dict(workload=f"mxfp8_w8a8_gemv_M{M}_N{N}_K{K}_blk32" + ("_rowmajor" if rowmajor else ""),
+    out = dict(workload=f"mxfp8_w8a8_gemv_M{M}_N{N}_K{K}_blk32" + ("_rowmajor" if rowmajor else "")
+               + ("_ceil448" if rule != mx.MX_RULE_OCP else ""),
                M=M, N=N, K=K, bytes_per_step=alg, weight_copies=nc, ms_per_step=ms_step,
                ms_kernel=ms_k, value=alg / (ms_step * 1e-3) / 1e9, unit="GB/s",
                kernel_gbs=alg / (ms_k * 1e-3) / 1e9, kernel=kname, step=how,
@@ -326,10 +331,12 @@ def bench_moe_block(torch, mx, g, wl, steps, warmup):
                 step="mx_moe_gate_up + mx_moe_down (combine)", src="mx_gemv.hip")
 
 
-def bench_gemm(torch, mx, g, wl, steps, warmup):
+def bench_gemm(torch, mx, g, wl, steps, warmup, rule=None):
     """Prefill W8A8 GEMM, M = 4096, N = K = 7168: per step one mx_linear with
     the activation quantized inside the call (T16 layout) then the GEMM; the
-    kernel-only timing runs the GEMM on a pre-quantized T16 activation."""
+    kernel-only timing runs the GEMM on a pre-quantized T16 activation.
+    rule: the activation scale rule of the step (default OCP)."""
+    rule = mx.MX_RULE_OCP if rule is None else rule
     d = wl.linear_inputs(5)
     N, K, M = d["N"], d["K"], d["M"]
     wp, cp = g.pack(0, 1, 1, N, K, d["w"], d["codes"])
@@ -343,7 +350,7 @@ def bench_gemm(torch, mx, g, wl, steps, warmup):
     mx.mx_quant_act_t16(M, K, x, K, xq, xc, mx.MX_RULE_OCP)
 
     def step(i):
-        mx.mx_linear(0, 1, N, K, wp, cp, M, mx.MX_ACT_MXFP8, mx.MX_RULE_OCP, x, K, None, 0,
+        mx.mx_linear(0, 1, N, K, wp, cp, M, mx.MX_ACT_MXFP8, rule, x, K, None, 0,
                      None, 0, None, y, N, ws, need)
 
     def kernel(i):
@@ -354,11 +361,13 @@ def bench_gemm(torch, mx, g, wl, steps, warmup):
     ms_step = timer.time(step, steps, warmup)
     ms_k = timer.time(kernel, steps, warmup)
     flop = 2.0 * M * N * K
-    return dict(workload=wl.WORKLOADS[5]["name"], M=M, N=N, K=K, flop_per_step=flop,
+    rname = "OCP rule" if rule == mx.MX_RULE_OCP else "ceil(log2(amax/448)) rule"
+    return dict(workload=wl.WORKLOADS[5]["name"] + ("_ceil448" if rule != mx.MX_RULE_OCP else ""),
+                M=M, N=N, K=K, flop_per_step=flop,
                 ms_per_step=ms_step, ms_kernel=ms_k, value=flop / (ms_step * 1e-3) / 1e12,
                 unit="TFLOP/s", kernel_tflops=flop / (ms_k * 1e-3) / 1e12,
                 kernel="gemm_w8a8_kernel (BLK32, T16 activations)",
-                step="mx_linear with in-call MXFP8 quantization (OCP rule)", src="mx_gemm.hip")
+                step=f"mx_linear with in-call MXFP8 quantization ({rname})", src="mx_gemm.hip")
 
 
 def cpu_baseline(wl):
@@ -435,6 +444,14 @@ def main():
             sec.append(bench_moe_block(torch, mx, g, wl, K, W)); log(json.dumps(sec[-1]))
         if want("gemm"):
             sec.append(bench_gemm(torch, mx, g, wl, max(10, K // 4), max(3, W // 4)))
+            log(json.dumps(sec[-1]))
+        # the pages' own scale rule, ceil(log2(amax / 448)), on the same two steps
+        if want("gemv16_ceil"):
+            sec.append(bench_w8a8_gemv(torch, mx, g, wl, 16, K, W, rule=mx.MX_RULE_CEIL448))
+            log(json.dumps(sec[-1]))
+        if want("gemm_ceil"):
+            sec.append(bench_gemm(torch, mx, g, wl, max(10, K // 4), max(3, W // 4),
+                                  rule=mx.MX_RULE_CEIL448))
             log(json.dumps(sec[-1]))
     if head is None:
         head = sec[0]
