@@ -381,8 +381,9 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_even_kernel(GemvW8Args p) {
 //
 // Order: the raw activations of all the wavefront's steps first (L2 hits,
 // they arrive long before the weights), then the weight chunks of the first
-// step and the weight codes; each step is quantized just before its MFMAs,
-// after which the next step's weight chunks are requested.  One step of
+// step and the weight codes; each step is quantized just before its MFMAs
+// (its LDS transpose one step earlier), after which the next step's weight
+// chunks are requested.  One step of
 // weight chunks in flight per wavefront (1,792 wavefronts, 7 MB in flight)
 // measured fastest on MI355X: deeper windows, and activations requested with
 // the weights of their step instead of all first, were slower.  Results are
@@ -479,16 +480,30 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
     v4f acc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g] = v4f{0.f, 0.f, 0.f, 0.f};
-    static_for<0, SPW>([&](auto iconst) {
-        constexpr int i = decltype(iconst)::value;
+    // The transpose runs one step ahead: step i + 1's tile write is queued
+    // behind step i's operand reads (a wavefront's LDS operations run in
+    // order) and its operand reads go out before step i's MFMAs, so the LDS
+    // round trip overlaps the quantization and the matrix cores.
+    const uint8_t *mine = tile + r * XROW + 32 * j;
+    auto put = [&](int i) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
             *reinterpret_cast<v4u *>(tile + (4 * u + j) * XROW + 16 * r) = xv[i][u];
-        const uint8_t *mine = tile + r * XROW + 32 * j;
-        const v4u f0 = *reinterpret_cast<const v4u *>(mine);
-        const v4u f1 = *reinterpret_cast<const v4u *>(mine + 16);
-        const v4u f2 = *reinterpret_cast<const v4u *>(mine + 128);
-        const v4u f3 = *reinterpret_cast<const v4u *>(mine + 144);
+    };
+    v4u f[4], fn[4];
+    auto get = [&](v4u (&d)[4]) {
+        d[0] = *reinterpret_cast<const v4u *>(mine);
+        d[1] = *reinterpret_cast<const v4u *>(mine + 16);
+        d[2] = *reinterpret_cast<const v4u *>(mine + 128);
+        d[3] = *reinterpret_cast<const v4u *>(mine + 144);
+    };
+    put(0);
+    get(f);
+    static_for<0, SPW>([&](auto iconst) {
+        constexpr int i = decltype(iconst)::value;
+        if constexpr (i + 1 < SPW) put(i + 1);
+        const v4u f0 = f[0], f1 = f[1], f2 = f[2], f3 = f[3];
+        if constexpr (i + 1 < SPW) get(fn);
         uint32_t c0, c1;
         const v4u q0 = quant_half_block_cvt<RULE>(f0, f1, c0);
         const v4u q1 = quant_half_block_cvt<RULE>(f2, f3, c1);
@@ -503,6 +518,10 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
         // the refill goes out right behind this step's MFMAs (left alone,
         // the scheduler sinks it next to its use and exposes its latency)
         if constexpr (i + WIN < SPW) wload(i + WIN);
+        if constexpr (i + 1 < SPW) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) f[c] = fn[c];
+        }
         __builtin_amdgcn_sched_barrier(0);
     });
 
