@@ -27,8 +27,16 @@ K = 1568), the A16W4 grouped MoE GEMV (E = 32, N = K = 3072, 16 tokens
 top-8) and the prefill W8A8 GEMM (M = 4096, N = K = 7168, quantization +
 GEMM per step; TFLOP/s against the 5.0 PFLOP/s fp8 peak).
 
+Timing: each workload's steps are captured in a HIP graph.  The warm-up
+graph (the requested number of steps) is replayed until at least
+WARM_MS milliseconds of GPU work have run, so clocks have settled after the
+idle seconds of input setup whatever --warmup says; then the graph of exactly
+`steps` steps is replayed REPLAYS times, each replay bracketed by synchronize
+and HIP events on the launch stream, and the median is reported.
+
 cpu_baseline: the CPU oracle (fp64, OpenMP) computing the headline step on
-the host cores, timed on the full workload, repeated for about 12 s.
+the host cores: on every thread for about 8 s (`value`, `cores`), and on one
+thread (`single_thread_value`), with the CPU model from /proc/cpuinfo.
 """
 from __future__ import annotations
 
@@ -46,6 +54,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 CACHE_BYTES = 512 << 20          # rotate at least this many bytes of weights
+WARM_MS = 200.0                  # least GPU time of warm-up replays per workload
+REPLAYS = 5                      # timed replays of the steps graph; the median is reported
 
 
 def parse():
@@ -94,6 +104,7 @@ class GraphTimer:
         return g
 
     eager = False
+    warm_ms = 0.0                      # the longest warm-up any workload took (ms of GPU time)
 
     def time(self, fn, steps, warmup):
         """ms per call of fn(i), over `steps` calls replayed back to back."""
@@ -109,15 +120,31 @@ class GraphTimer:
             return (time.perf_counter() - t) * 1e3 / steps
         gw = self._graph(fn, max(warmup, 1))
         gt = self._graph(fn, steps)
-        gw.replay()
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        gt.replay()
-        t1.record()
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / steps
+        # warm-up: the requested steps, replayed until WARM_MS of GPU time
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        warm = 0.0
+        while True:
+            e0.record()
+            gw.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            warm += e0.elapsed_time(e1)
+            if warm >= WARM_MS:
+                break
+        GraphTimer.warm_ms = max(GraphTimer.warm_ms, warm)
+        times = []
+        for _ in range(REPLAYS):
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0.record()
+            gt.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            times.append(t0.elapsed_time(t1) / steps)
+        times.sort()
+        return times[len(times) // 2]
 
     def run(self, step, kernel, steps, warmup):
         """(ms per step, ms per launch of the dominant kernel alone)."""
@@ -370,22 +397,47 @@ def bench_gemm(torch, mx, g, wl, steps, warmup, rule=None):
                 step=f"mx_linear with in-call MXFP8 quantization ({rname})", src="mx_gemm.hip")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl):
+    """The oracle, as it stands, computing the headline step (per-token
+    quantization of M = 16 rows, then the fp64 linear with N = K = 7168) on
+    every host thread for about 8 s, then on one thread (a few runs)."""
     import oracle
     d = wl.linear_inputs(2, M=16)
     N, K = d["N"], d["K"]
     alg = N * K + (N // 32) * (K // 32)
-    runs, t_total = 0, 0.0
-    while t_total < 12.0 and runs < 2000:
-        t = time.perf_counter()
-        xq, xc = oracle.quant_act(d["x"], oracle.RULE_OCP)
-        oracle.linear(0, 1, N, K, d["w"], d["codes"], 16, oracle.ACT_MXFP8, xq=xq, xcodes=xc)
-        t_total += time.perf_counter() - t
-        runs += 1
-    sec = t_total / runs
-    return {"value": alg / sec / 1e9, "unit": "GB/s", "cores": oracle.threads(), "kind": "oracle",
+
+    def run(budget_s, max_runs):
+        runs, t_total = 0, 0.0
+        while (t_total < budget_s or runs < 1) and runs < max_runs:
+            t = time.perf_counter()
+            xq, xc = oracle.quant_act(d["x"], oracle.RULE_OCP)
+            oracle.linear(0, 1, N, K, d["w"], d["codes"], 16, oracle.ACT_MXFP8, xq=xq, xcodes=xc)
+            t_total += time.perf_counter() - t
+            runs += 1
+        return runs, t_total / runs
+
+    cores = oracle.threads()
+    runs, sec = run(8.0, 2000)
+    prev = oracle.set_threads(1)
+    try:
+        runs1, sec1 = run(4.0, 8)
+    finally:
+        oracle.set_threads(prev)
+    return {"value": alg / sec / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"the full headline step (M=16, N=K=7168: quant + fp64 linear), "
-                      f"{runs} runs, {sec:.2f} s each"}
+                      f"{runs} runs on {cores} threads, {sec:.3f} s each; "
+                      f"{runs1} runs on 1 thread, {sec1:.2f} s each",
+            "single_thread_value": alg / sec1 / 1e9, "cpu_model": cpu_model()}
 
 
 def main():
@@ -480,6 +532,8 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
+        "warmup_ms": round(GraphTimer.warm_ms, 1),
+        "timed_replays": REPLAYS,
         "ms_per_step": round(head["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -6,6 +6,7 @@
  *   [weights942]   vllm.models.deepseek_v41.amd.mono.weights942
  *   [rocm_native]  vllm.model_executor.kernels.linear.mxfp8.rocm_native
  *   [a16w4]        vllm.models.minimax_m3.amd.specialized_decode.mono.a16w4
+ *   [fused_layout] vllm.models.deepseek_v41.common.ops.fused_layout
  *
  * Number formats.
  *   E4M3   OCP fp8 byte (bias 7, max 448, 0x7F/0xFF NaN)        [weights942]
@@ -107,6 +108,10 @@ typedef enum { MX_ACT_BF16 = 0, MX_ACT_MXFP8 = 1, MX_ACT_MXFP8_T16 = 2 } mx_act;
  *          byte 4 l + u = code[e N + 16 t + r][4 (4 q + u) + j].
  *   BLK32: 16 bytes per (32-row group R, q) at (R Q + q) * 16, R < E N / 32;
  *          byte 4 j + u = code[R][4 (4 q + u) + j].
+ *   Then a 16-byte trailer: byte 0 is the smallest and byte 1 the largest of
+ *   the codes given to the pack (padding codes not counted), bytes 2..15
+ *   are 0.  The bf16-activation products read it to learn whether every
+ *   scaled weight is a normal bf16 number (below).
  * Each lane group j reads one dword per quad of steps, whose byte u is the
  * code of step 4 q + u: the scaled MFMA's byte select picks it directly.
  */
@@ -235,6 +240,13 @@ mx_status mx_linear_workspace(int elem, int layout, int64_t N, int64_t K,
 
 /* y[M, N] = a . Wf^T (+ bias), bf16 out, fp32 accumulation, one final
  * round to nearest-even bf16 ([rocm_native] apply_weights).
+ * Every E8M0 code 0 .. 254 is served exactly on every path: products and
+ * partial sums are formed without loss wherever they lie in fp32's normal
+ * range.  With bf16 activations the weights are decoded to bf16 with their
+ * scale; when a code lies outside 10 .. 246 (E4M3) or 2 .. 252 (E2M1), where
+ * a scaled weight would leave bf16's normal range, that work is done on each
+ * 32-K block's partial with the scale applied in fp32 instead (slower; such
+ * codes mean weights beyond 2^120 or below 2^-117).
  *   Wf[n][k] = dec(W[n][k]) * 2^(code(n, k) - 127) from the packed buffers.
  *   a = x (bf16) when act == MX_ACT_BF16;
  *   a = dec(xq) * 2^(xcode - 127) when act == MX_ACT_MXFP8: if xq and xcodes
@@ -297,7 +309,8 @@ mx_status mx_moe_linear(int elem, int64_t E, int64_t N, int64_t K,
  *   w2  (device) [E, H, Np values] (Np/2 or Np bytes a row), zero beyond
  *       inter;  s2 (device) codes [E, H, Np/32].
  * Output (device, caller-owned, 16-byte aligned):
- *   w13_out [E, 2 inter, rowb] with gate row i at 2 i and up row i at 2 i + 1,
+ *   w13_out [E, 2 inter, rowb]: gate and up rows interleaved, the even row
+ *       2 i holding gate row i and the odd row after it up row i,
  *   s13_out [E, 2 inter, K/32] alike, w2_out [E, H, inter values],
  *   s2_out [E, H, inter/32].
  * Bytes are copied verbatim (-0 nibbles kept).  Then pack them with

@@ -233,7 +233,8 @@ mx_status mx_packed_sizes(int elem, int layout, int64_t E, int64_t N, int64_t K,
     if (st != MX_OK) return st;
     const int64_t Kp = padded_k(K), S = Kp / 128, Q = (S + 3) / 4;
     *w_bytes = (size_t)(E * N * (elem == E4M3 ? K : K / 2));   // no stored padding
-    *code_bytes = (size_t)(layout == ROW32 ? E * (N / 16) * Q * 256 : E * (N / 32) * Q * 16);
+    *code_bytes = (size_t)(mx::packed_code_body_bytes(layout, E, N, K) + mx::kCodeTrailer);
+    (void)Q;
     return MX_OK;
 }
 
@@ -250,16 +251,29 @@ mx_status mx_pack_weights(int elem, int layout, int64_t E, int64_t N, int64_t K,
     if (ws_bytes < 256) return MX_ERR_WORKSPACE;
     if ((st = device_ok()) != MX_OK) return st;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // ws: the code-255 flag, then the code range's two counters (255, 0)
     int *bad = static_cast<int *>(ws);
-    if (hipMemsetAsync(bad, 0, sizeof(int), s) != hipSuccess) return MX_ERR_LAUNCH;
+    unsigned *range = reinterpret_cast<unsigned *>(static_cast<uint8_t *>(ws) + 4);
+    if (hipMemsetAsync(bad, 0, 12, s) != hipSuccess ||
+        hipMemsetAsync(range, 0xFF, 1, s) != hipSuccess)
+        return MX_ERR_LAUNCH;
     if ((st = launched(mx::launch_pack(elem, layout, E, N, K, w, codes, w_packed, codes_packed,
-                                       bad, s))) != MX_OK)
+                                       bad, range, s))) != MX_OK)
         return st;
-    int h = 0;
-    if (hipMemcpyAsync(&h, bad, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess ||
+    int h[3] = {0, 0, 0};
+    if (hipMemcpyAsync(h, bad, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)
         return MX_ERR_LAUNCH;
-    return h ? MX_ERR_VALUE : MX_OK;
+    if (h[0]) return MX_ERR_VALUE;
+    // the trailer after the packed codes: smallest and largest given code
+    uint8_t trailer[mx::kCodeTrailer] = {};
+    trailer[0] = (uint8_t)h[1];
+    trailer[1] = (uint8_t)h[2];
+    uint8_t *tail = static_cast<uint8_t *>(codes_packed) + (cb - mx::kCodeTrailer);
+    if (hipMemcpyAsync(tail, trailer, sizeof(trailer), hipMemcpyHostToDevice, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return MX_ERR_LAUNCH;
+    return MX_OK;
 }
 
 mx_status mx_quant_act(int64_t M, int64_t K, const void *x, int64_t ldx, void *xq, int64_t ldq,

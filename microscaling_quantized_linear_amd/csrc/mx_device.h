@@ -67,8 +67,9 @@ __device__ inline float code_as_scale(uint32_t code) { return __uint_as_float(co
 
 __device__ inline uint32_t byte_of(uint32_t w, uint32_t i) { return (w >> (8 * i)) & 0xFFu; }
 
-// 8 e4m3 bytes (two dwords) x 2^(code-127) -> 8 bf16 (exact for codes whose
-// products stay inside bf16's normal range; rounded to nearest otherwise).
+// 8 e4m3 bytes (two dwords) x 2^(code-127) -> 8 bf16: exact while every
+// product is a normal bf16 number (codes 10 .. 246); callers apply the rest
+// of a code outside that range in fp32 (a16_exact_tile).
 __device__ inline v8bf dec8_e4m3(uint32_t w0, uint32_t w1, float scale) {
     v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, false);
     v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, scale, true);
@@ -79,7 +80,7 @@ __device__ inline v8bf dec8_e4m3(uint32_t w0, uint32_t w1, float scale) {
 }
 
 // 8 e2m1 nibbles (one dword, low nibble first) x 2^(code-127) -> 8 bf16
-// ([a16w4] dequant: four scaled pair conversions).
+// ([a16w4] dequant: four scaled pair conversions); exact for codes 2 .. 252.
 __device__ inline v8bf dec8_e2m1(uint32_t w, float scale) {
     v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
     v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);

@@ -25,8 +25,8 @@
 // any weight byte if there are none.  Two runtime modes serve the MoE block:
 // `xslot` reads one activation row per slot (the down projection of the
 // hidden rows), `epi` turns interleaved (gate, up) row pairs into
-// silu(gate) * up, one output per pair ([weights942] moe_copies pairs gate
-// row i with up row i at rows 2 i, 2 i + 1).
+// silu(gate) * up, one output per pair ([weights942] moe_copies interleaves
+// the two halves: even rows gate, odd rows up).
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -43,6 +43,62 @@ struct StepA16 {
     v4u x0, x1, x2, x3;   // bf16 activations of the four MFMAs
     uint32_t cw[G], cw2[G];
 };
+
+// One tile's step of the A16 product in exact form, for steps holding an E8M0
+// code outside kLo .. kHi (the range where every scaled weight is a normal
+// bf16 number): decode with the code clamped into that range, take each
+// 32-K block's partial on its own (the operands of the lane groups that do
+// not hold the block are zero), multiply the partial by the remaining power
+// of two 2^(code - clamped) in fp32 and add it to acc.  Output row 4 j + i of
+// a lane takes the factor of that row's block, read from the lanes whose
+// weight row it is.  Lane (r, j) holds, for its row r: E4M3 a0 = K 16 j ..
+// (block j / 2, code c0) and a1 = K 64 + 16 j .. (block 2 + j / 2, code c1);
+// E2M1 a0 = block j (code c0).  All 64 lanes must be active.
+template <int ELEM>
+__device__ inline v4f a16_exact_tile(v4f acc, v4u a0, v4u a1, v4u x0, v4u x1,
+                                                       v4u x2, v4u x3, uint32_t c0, uint32_t c1,
+                                                       int j) {
+    constexpr uint32_t kLo = ELEM == E4M3 ? 10u : 2u, kHi = ELEM == E4M3 ? 246u : 252u;
+    const uint32_t k0 = c0 < kLo ? kLo : (c0 > kHi ? kHi : c0);
+    const uint32_t k1 = c1 < kLo ? kLo : (c1 > kHi ? kHi : c1);
+    const int d0 = (int)c0 - (int)k0, d1 = (int)c1 - (int)k1;
+    const float f0 = code_as_scale(k0), f1 = code_as_scale(k1);
+    const v4u xx[4] = {x0, x1, x2, x3};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        // E4M3: block b sits in operands 2 (b / 2), + 1 of lane groups
+        // 2 (b % 2), + 1 (half b / 2: code c0 or c1); E2M1: in all four
+        // operands of lane group b
+        v4f t = {0.f, 0.f, 0.f, 0.f};
+        int delta;
+        if (ELEM == E4M3) {
+            const bool mine = j / 2 == b % 2;
+            const int h = b / 2;
+            const v4u a = h ? a1 : a0;
+            const float f = h ? f1 : f0;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const uint32_t lo = mine ? a[2 * q] : 0u, hi = mine ? a[2 * q + 1] : 0u;
+                t = mfma_bf16(dec8_e4m3(lo, hi, f), as_bf16x8(xx[2 * h + q]), t);
+            }
+            delta = h ? d1 : d0;
+        } else {
+            const bool mine = j == b;
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                t = mfma_bf16(dec8_e2m1(mine ? a0[d] : 0u, f0), as_bf16x8(xx[d]), t);
+            delta = d0;
+        }
+        const int src0 = ELEM == E4M3 ? 32 * (b % 2) : 16 * b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int di = __shfl(delta, src0 + 4 * j + i);
+            acc[i] += t[i] * __uint_as_float((uint32_t)(127 + di) << 23);
+        }
+        __builtin_amdgcn_sched_barrier(0);      // one block's temporaries at a time
+    }
+    return acc;
+}
 
 // G: weight tiles per workgroup.  A wavefront's activation fragment of a step
 // is loaded once and feeds the G tiles' matrix-core operations.
@@ -91,6 +147,18 @@ gemv_kernel(GemvArgs p) {
 
     const int64_t s0 = (wave * S) / NW, s1 = ((wave + 1) * S) / NW;
 
+    // A16: is any weight code outside kLo .. kHi?  The register-tight grouped
+    // A16W4 GEMV reads the tensor's code range from the packed codes' trailer
+    // (one scalar load; its wait lands ahead of the first loads, which that
+    // kernel's routing scan pays anyway); the others note the codes of their
+    // own steps as the loop meets them.
+    constexpr uint32_t kLo = ELEM == E4M3 ? 10u : 2u, kHi = ELEM == E4M3 ? 246u : 252u;
+    constexpr bool kRangeTrailer = MOE && ELEM == E2M1;
+    uint32_t crange = 0;
+    if (ACT == ACT_BF16 && kRangeTrailer)
+        crange = *reinterpret_cast<const uint32_t *>(
+            p.codes + packed_code_body_bytes(LAYOUT, p.E, p.N, p.K));
+
     // weight and code offsets of tile g at step s (out of range beyond s1,
     // and past the last step's valid prefix); half 1 is an E4M3 chunk's
     // second 1 KB
@@ -99,12 +167,15 @@ gemv_kernel(GemvArgs p) {
         if (!in || (s == S - 1 && o >= tailb)) return kOOB;
         return (uint32_t)(g * TILEB + s * CHUNK) + o;
     };
-    // the dword holding this step's code of the lane's row for lane group jj
-    // (byte s % 4 of it): ROW32 the lane's own C-T16 dword, BLK32 dword jj of
-    // the row group's 16-byte quad
+    // the dword holding this step's code of the lane's row r for the block
+    // of lane group jj (byte s % 4 of it): ROW32 the C-T16 dword of lane
+    // 16 jj + r (only the A16 e4m3 form asks for jj != j; the others read the
+    // lane's own), BLK32 dword jj of the row group's 16-byte quad
     auto coff = [&](int g, int64_t s, bool in, int jj) -> uint32_t {
         if (!in) return kOOB;
-        if (LAYOUT == ROW32) return (uint32_t)((g * Q + s / 4) * 256 + 4 * lane);
+        if (LAYOUT == ROW32)
+            return (uint32_t)((g * Q + s / 4) * 256 +
+                              (ELEM == E4M3 && ACT == ACT_BF16 ? 4 * (16 * jj + r) : 4 * lane));
         return crow[g] + (uint32_t)((s / 4) * 16 + 4 * jj);
     };
 
@@ -120,7 +191,10 @@ gemv_kernel(GemvArgs p) {
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            if (ELEM == E4M3 && LAYOUT == BLK32) {
+            if (ELEM == E4M3) {
+                // codes of the blocks holding K 16 j.. (block j / 2) and
+                // 64 + 16 j.. (block 2 + j / 2) of this lane's row, loaded
+                // directly (no lane exchange in the loop)
                 st.cw[g] = load4(cr, coff(g, s, in, j / 2));
                 st.cw2[g] = load4(cr, coff(g, s, in, 2 + j / 2));
             } else {
@@ -234,7 +308,7 @@ gemv_kernel(GemvArgs p) {
             }
         } else {
             // ---- A16: bf16 activations, weights decoded in registers ----
-            auto loadx = [&](StepA16<G> &st, int64_t s) {
+            auto loadx = [&](auto &st, int64_t s) {
                 const bool in = s < s1;
                 if (ELEM == E4M3) {
                     // MFMA d covers K 16 j + 8 d (d < 2) and 64 + 16 j + 8 (d - 2)
@@ -258,38 +332,45 @@ gemv_kernel(GemvArgs p) {
                 loadx(st, s);
                 return st;
             };
+            // Each lane's weight bytes belong to one 32-K block per 16-byte
+            // half (E4M3: K 16 j .. is block j / 2, K 64 + 16 j .. block
+            // 2 + j / 2; E2M1: the lane's 16 bytes are block j), so one code
+            // per half scales them.  Decoded with that code the bf16 operand
+            // is exact while every e4m3 / e2m1 value times 2^(code - 127)
+            // stays in bf16's normal range (codes kLo .. kHi).  The loop
+            // assumes so; when a code leaves kLo .. kHi (see kRangeTrailer)
+            // the wavefront's range is done again in the exact form
+            // (a16_exact_tile) after the loop.
+            auto codes_of = [&](uint32_t cw, uint32_t cw2, int64_t s, uint32_t &c0,
+                                uint32_t &c1) {
+                const uint32_t u = (uint32_t)(s % 4);
+                c0 = byte_of(cw, u);
+                c1 = ELEM == E4M3 ? byte_of(cw2, u) : c0;
+            };
+            bool outside = false;             // a code of this lane's steps outside kLo .. kHi
             auto compute = [&](const StepA16<G> &st, int64_t s) {
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
+                    uint32_t c0, c1;
+                    codes_of(st.cw[g], st.cw2[g], s, c0, c1);
+                    // (steps past s1 read code 0 and zero bytes: not counted)
+                    if (!kRangeTrailer)
+                        outside = outside ||
+                                  (s < s1 && (c0 - kLo > kHi - kLo || c1 - kLo > kHi - kLo));
+                    const float f0 = code_as_scale(c0), f1 = code_as_scale(c1);
+                    v4f c = acc[g];
                     if (ELEM == E4M3) {
-                        // codes of the blocks holding K 16 j.. (block j/2) and
-                        // 64 + 16 j.. (block 2 + j/2) of this lane's row
-                        uint32_t c0, c1;
-                        if (LAYOUT == ROW32) {
-                            const uint32_t u = (uint32_t)(s % 4);
-                            c0 = byte_of((uint32_t)__shfl((int)st.cw[g], 16 * (j / 2) + r), u);
-                            c1 = byte_of((uint32_t)__shfl((int)st.cw[g], 16 * (2 + j / 2) + r), u);
-                        } else {
-                            c0 = byte_of(st.cw[g], (uint32_t)(s % 4));
-                            c1 = byte_of(st.cw2[g], (uint32_t)(s % 4));
-                        }
-                        const float f0 = code_as_scale(c0), f1 = code_as_scale(c1);
-                        v4f c = acc[g];
                         c = mfma_bf16(dec8_e4m3(st.a0[g][0], st.a0[g][1], f0), as_bf16x8(st.x0), c);
                         c = mfma_bf16(dec8_e4m3(st.a0[g][2], st.a0[g][3], f0), as_bf16x8(st.x1), c);
                         c = mfma_bf16(dec8_e4m3(st.a1[g][0], st.a1[g][1], f1), as_bf16x8(st.x2), c);
                         c = mfma_bf16(dec8_e4m3(st.a1[g][2], st.a1[g][3], f1), as_bf16x8(st.x3), c);
-                        acc[g] = c;
                     } else {
-                        const uint32_t cc = byte_of(st.cw[g], (uint32_t)(s % 4));
-                        const float f = code_as_scale(cc);
-                        v4f c = acc[g];
-                        c = mfma_bf16(dec8_e2m1(st.a0[g][0], f), as_bf16x8(st.x0), c);
-                        c = mfma_bf16(dec8_e2m1(st.a0[g][1], f), as_bf16x8(st.x1), c);
-                        c = mfma_bf16(dec8_e2m1(st.a0[g][2], f), as_bf16x8(st.x2), c);
-                        c = mfma_bf16(dec8_e2m1(st.a0[g][3], f), as_bf16x8(st.x3), c);
-                        acc[g] = c;
+                        c = mfma_bf16(dec8_e2m1(st.a0[g][0], f0), as_bf16x8(st.x0), c);
+                        c = mfma_bf16(dec8_e2m1(st.a0[g][1], f0), as_bf16x8(st.x1), c);
+                        c = mfma_bf16(dec8_e2m1(st.a0[g][2], f0), as_bf16x8(st.x2), c);
+                        c = mfma_bf16(dec8_e2m1(st.a0[g][3], f0), as_bf16x8(st.x3), c);
                     }
+                    acc[g] = c;
                 }
             };
             for (int64_t c = s0; c < s1; c += P) {
@@ -299,6 +380,41 @@ gemv_kernel(GemvArgs p) {
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int u = 0; u < P; ++u) compute(st[u], c + u);
+            }
+            const bool exact = kRangeTrailer
+                                   ? (crange & 0xFFu) < kLo || ((crange >> 8) & 0xFFu) > kHi
+                                   : __any(outside);
+            if (exact) {
+                // exact form, one tile and step at a time on reloaded
+                // operands; the partial tiles live in this wavefront's slot
+                // of the reduction buffer meanwhile (fewer registers)
+                v4f *part = red[NW > 1 ? wave : 0][0] + lane;      // tile g at part[64 g]
+#pragma unroll
+                for (int g = 0; g < G; ++g) part[64 * g] = v4f{0.f, 0.f, 0.f, 0.f};
+                for (int64_t s = s0; s < s1; ++s) {
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        StepA16<1> one;
+                        one.a0[0] = load16<kNT>(wr, woff(g, s, true, 0));
+                        one.a1[0] = ELEM == E4M3 ? load16<kNT>(wr, woff(g, s, true, 1)) : v4u{};
+                        if (ELEM == E4M3) {
+                            one.cw[0] = load4(cr, coff(g, s, true, j / 2));
+                            one.cw2[0] = load4(cr, coff(g, s, true, 2 + j / 2));
+                        } else {
+                            one.cw[0] = load4(cr, coff(g, s, true, j));
+                            one.cw2[0] = 0;
+                        }
+                        loadx(one, s);
+                        uint32_t c0, c1;
+                        codes_of(one.cw[0], one.cw2[0], s, c0, c1);
+                        part[64 * g] = a16_exact_tile<ELEM>(part[64 * g], one.a0[0],
+                                                            ELEM == E4M3 ? one.a1[0] : one.a0[0],
+                                                            one.x0, one.x1, one.x2, one.x3, c0, c1, j);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                }
+#pragma unroll
+                for (int g = 0; g < G; ++g) acc[g] = part[64 * g];
             }
         }
 

@@ -56,8 +56,20 @@ hipError_t launch_act_codes_t16(int64_t M, int64_t K, const void *xc, int64_t ld
 hipError_t launch_act_data_t16(int64_t M, int64_t K, const void *xq, int64_t ldq, void *out,
                                hipStream_t stream);
 
+// range: two unsigned counters the codes' smallest / largest value is folded
+// into (atomic min / max); the caller sets them to 255 / 0 first
 hipError_t launch_pack(int elem, int layout, int64_t E, int64_t N, int64_t K, const void *w,
-                       const void *codes, void *wp, void *cp, int *bad, hipStream_t stream);
+                       const void *codes, void *wp, void *cp, int *bad, unsigned *range,
+                       hipStream_t stream);
+
+// Bytes of packed codes before the 16-byte code-range trailer (byte 0: the
+// smallest given code, byte 1: the largest; padding codes not counted).
+__host__ __device__ inline int64_t packed_code_body_bytes(int layout, int64_t E, int64_t N,
+                                                          int64_t K) {
+    const int64_t S = (K + 127) / 128, Q = (S + 3) / 4;
+    return layout == 0 ? E * (N / 16) * Q * 256 : E * (N / 32) * Q * 16;
+}
+constexpr int64_t kCodeTrailer = 16;
 // [weights942] moe_copies: the padding check (sets *bad), then the copies
 hipError_t launch_moe_padding_check(int elem, int64_t E, int64_t Np, int64_t inter, int64_t K,
                                     int64_t H, const void *w13, const void *w2, int *bad,

@@ -48,15 +48,18 @@ __global__ void __launch_bounds__(256) pack_weights_kernel(
 }
 
 // ROW32: one thread writes one dword (4 codes) of C-T16.  BLK32: one byte.
-// Any code 255 sets *bad.
+// Any code 255 sets *bad; range[0] / range[1] collect the smallest and the
+// largest given code (padding not counted) for the trailer.
 __global__ void __launch_bounds__(256) pack_codes_kernel(
     int layout, int64_t E, int64_t N, int64_t K, const uint8_t *__restrict__ codes,
-    uint8_t *__restrict__ cp, int64_t nunits, int *__restrict__ bad) {
+    uint8_t *__restrict__ cp, int64_t nunits, int *__restrict__ bad,
+    unsigned *__restrict__ range) {
     int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (p >= nunits) return;
     const int64_t KB = K / 32, Kp = (K + 127) / 128 * 128, S = Kp / 128, Q = (S + 3) / 4;
     const int64_t T = N / 16;
     int found = 0;
+    unsigned lo = 255, hi = 0;
+    if (p < nunits) {
     if (layout == ROW32) {
         const int64_t lane = p % 64, etq = p / 64;
         const int64_t q = etq % Q, et = etq / Q;
@@ -68,6 +71,8 @@ __global__ void __launch_bounds__(256) pack_codes_kernel(
             if (blk < KB) {
                 c = codes[row * KB + blk];
                 found |= c == 255;
+                lo = c < lo ? c : lo;
+                hi = c > hi ? c : hi;
             }
             dw |= c << (8 * u);
         }
@@ -82,10 +87,23 @@ __global__ void __launch_bounds__(256) pack_codes_kernel(
         if (b < KB) {
             c = codes[R * KB + b];
             found = c == 255;
+            lo = hi = c;
         }
         cp[p] = (uint8_t)c;
     }
+    }
     if (found) atomicOr(bad, 1);
+    // the wavefront's range, then one pair of atomics per wavefront
+#pragma unroll
+    for (int d = 32; d >= 1; d /= 2) {
+        const unsigned olo = (unsigned)__shfl_xor((int)lo, d), ohi = (unsigned)__shfl_xor((int)hi, d);
+        lo = olo < lo ? olo : lo;
+        hi = ohi > hi ? ohi : hi;
+    }
+    if (threadIdx.x % 64 == 0 && lo <= hi) {
+        atomicMin(&range[0], lo);
+        atomicMax(&range[1], hi);
+    }
 }
 
 // Row-major activation codes [M, ldc] -> XC-T16: per 16-row tile and quad of
@@ -146,7 +164,8 @@ hipError_t launch_act_data_t16(int64_t M, int64_t K, const void *xq, int64_t ldq
 }
 
 hipError_t launch_pack(int elem, int layout, int64_t E, int64_t N, int64_t K, const void *w,
-                       const void *codes, void *wp, void *cp, int *bad, hipStream_t stream) {
+                       const void *codes, void *wp, void *cp, int *bad, unsigned *range,
+                       hipStream_t stream) {
     const int64_t Kp = (K + 127) / 128 * 128, S = Kp / 128, Q = (S + 3) / 4;
     const int64_t wbytes = E * N * (elem == E4M3 ? K : K / 2);
     const int64_t npieces = wbytes / 16;
@@ -157,7 +176,7 @@ hipError_t launch_pack(int elem, int layout, int64_t E, int64_t N, int64_t K, co
     const int64_t nunits = layout == ROW32 ? E * (N / 16) * Q * 64 : E * (N / 32) * Q * 16;
     hipLaunchKernelGGL(pack_codes_kernel, dim3((unsigned)((nunits + 255) / 256)), dim3(256), 0,
                        stream, layout, E, N, K, (const uint8_t *)codes, (uint8_t *)cp, nunits,
-                       bad);
+                       bad, range);
     return hipGetLastError();
 }
 

@@ -91,6 +91,8 @@ def _declare(L):
     L.orc_fused_layout_permute.restype = i32
     L.orc_threads.argtypes = []
     L.orc_threads.restype = i32
+    L.orc_set_threads.argtypes = [i32]
+    L.orc_set_threads.restype = i32
 
 
 def _ptr(a):
@@ -255,7 +257,8 @@ def bf16_round_array(a: np.ndarray) -> np.ndarray:
 
 def moe_gate_up(elem, E, inter, K, w13, codes, x, ids):
     """fp64 h [T, topk, inter] = silu(x . gate^T) * (x . up^T) over the
-    interleaved expert rows (gate row i at 2 i, up row i at 2 i + 1)."""
+    interleaved expert rows (even row 2 i: gate row i; the odd row after it:
+    up row i)."""
     w13 = _c(w13, np.uint8)
     codes = _c(codes, np.uint8)
     x = _c(x, np.uint16)
@@ -345,3 +348,9 @@ def fused_layout_permute(kind, layout, N, K, heads, w, codes):
 def threads() -> int:
     """OpenMP threads the oracle's loops run on."""
     return lib().orc_threads()
+
+
+def set_threads(n: int) -> int:
+    """Run the oracle's loops on n OpenMP threads from now on; returns the
+    previous count."""
+    return lib().orc_set_threads(int(n))

@@ -280,6 +280,7 @@ int orc_packed_sizes(int elem, int layout, int64_t E, int64_t N, int64_t K,
         *c_bytes = E * (N / 16) * Q * 256;
     else
         *c_bytes = E * (N / 32) * Q * 16;
+    *c_bytes += 16;                                /* the code-range trailer */
     return 0;
 }
 
@@ -335,6 +336,19 @@ int orc_pack_weights(int elem, int layout, int64_t E, int64_t N, int64_t K,
                         int64_t dst = (R * Q + q) * 16 + 4 * jj + u;
                         cp[dst] = blk < K / 32 ? codes[R * (K / 32) + blk] : 128;
                     }
+    }
+    /* trailer: the smallest and the largest of the given codes (padding not
+     * counted), then 14 zero bytes */
+    {
+        int64_t n = (layout == ORC_ROW32 ? E * N : E * N / 32) * (K / 32), i;
+        uint8_t lo = 255, hi = 0;
+        for (i = 0; i < n; i++) {
+            if (codes[i] < lo) lo = codes[i];
+            if (codes[i] > hi) hi = codes[i];
+        }
+        memset(cp + cb - 16, 0, 16);
+        cp[cb - 16] = lo;
+        cp[cb - 15] = hi;
     }
     return 0;
 }
@@ -785,6 +799,21 @@ int orc_threads(void)
 #ifdef _OPENMP
     return omp_get_max_threads();
 #else
+    return 1;
+#endif
+}
+
+/* Sets the number of threads the OpenMP loops above use from now on (the
+ * benchmark's CPU baseline times one thread and all of them); returns the
+ * previous count.  Without OpenMP it does nothing and returns 1. */
+int orc_set_threads(int n)
+{
+#ifdef _OPENMP
+    const int prev = omp_get_max_threads();
+    if (n > 0) omp_set_num_threads(n);
+    return prev;
+#else
+    (void)n;
     return 1;
 #endif
 }

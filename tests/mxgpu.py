@@ -129,8 +129,12 @@ def bf16_ulp(v: np.ndarray) -> np.ndarray:
     return np.exp2(np.floor(np.log2(a)) - 7)
 
 
-def assert_close(y_bits: np.ndarray, ref: np.ndarray, what: str = ""):
+def assert_close(y_bits: np.ndarray, ref: np.ndarray, what: str = "", strict: bool = False):
     """The bar: relative L2 <= 2e-3 and every |err| <= 1e-2 * max|oracle row|.
+
+    strict: the relative-L2 bar holds as stated, with no fallback (the
+    full-size workloads have enough outputs that the rounding floor sits
+    well below 2e-3).
 
     Where the exact result rounded once to bf16 does not itself reach the
     2e-3 bar (cases with few outputs: the rounding floor of the relative L2
@@ -147,6 +151,7 @@ def assert_close(y_bits: np.ndarray, ref: np.ndarray, what: str = ""):
     nref = np.linalg.norm(ref)
     rel = np.linalg.norm(err) / nref if nref > 0 else np.linalg.norm(err)
     if rel > REL_L2:
+        assert not strict, f"{what}: relative L2 {rel:.3e} > {REL_L2}"
         floor = rounding_floor(ref)
         assert floor >= 0.95 * REL_L2, f"{what}: relative L2 {rel:.3e} > {REL_L2} (floor {floor:.3e})"
         rowmax1 = np.abs(ref.reshape(-1, ref.shape[-1])).max(axis=1, keepdims=True)

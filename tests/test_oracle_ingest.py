@@ -4,9 +4,9 @@ orc_fold_row_codes ([rocm_native] _as_block32_scale, [weights942]
 linear_copy) and orc_e4m3_from_dequant ([weights942] ocp_from_dequant) are
 checked against things other than themselves: brute force over all 65,536
 bf16 patterns and all finite e4m3 bytes, round trips whose bf16 weights come
-from torch's CPU cast, the page's own steps run as torch CPU ops (a library
-routine, run, not read), and the pinned dense linear of the oracle on folded
-and expanded codes."""
+from torch's CPU cast, the definition of exact recovery stated with numpy on
+a mix of representable and perturbed weights, and the pinned dense linear of
+the oracle on folded and expanded codes."""
 import numpy as np
 import pytest
 import torch
@@ -118,33 +118,35 @@ def test_from_dequant_round_trip_of_dequantized_bytes():
     assert got[tuple(i)] == 0xFF and (got != 0xFF).sum() == N * K - 1
 
 
-def test_from_dequant_agrees_with_the_pages_steps_in_torch():
-    """The page's steps as torch CPU ops (fp32 multiply, cast to e4m3fn,
-    divide, cast to bf16, compare) accept exactly the weights the oracle
-    accepts, with the same bytes, on a mix of exact and inexact weights."""
+def test_from_dequant_mixed_weights_by_definition():
+    """A mix of representable and perturbed bf16 weights under 32x32 codes:
+    a weight w is recovered exactly when w * 2^(127 - c), formed exactly in
+    binary64, is one of the finite e4m3 values (a zero keeping its sign), and
+    its byte is that value's; every other weight is refused (0xFF)."""
     rng = np.random.default_rng(84)
     N, K = 128, 128
     blk = wl.codes(rng, (N // 32, K // 32), 110, 140)
-    rows = np.repeat(blk, 32, axis=0)
+    c = np.repeat(np.repeat(blk, 32, axis=0), 32, axis=1).astype(np.int64)
     q = wl.e4m3_bytes(rng, (N, K))
     b, v = _e4m3_table()
     val = np.zeros(256)
     val[b] = v
-    scale = np.ldexp(1.0, rows.astype(np.int64) - 127).repeat(32, axis=1)
-    exact = val[q] * scale
+    exact = val[q] * np.ldexp(1.0, c - 127)
     noisy = exact * (1 + rng.standard_normal((N, K)) * 0.02)
-    pick = rng.random((N, K)) < 0.5
-    w = _torch_bf16_bits(np.where(pick, exact, noisy))
+    w = _torch_bf16_bits(np.where(rng.random((N, K)) < 0.5, exact, noisy))
     got = oracle.e4m3_from_dequant(BLK32, N, K, w, blk, strict=False)
-    wt = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16)
-    mul = torch.exp2(127.0 - torch.from_numpy(blk).float())
-    mul = mul.repeat_interleave(32, 0).repeat_interleave(32, 1)
-    qt = (wt.float() * mul).to(torch.float8_e4m3fn)
-    back = (qt.float() / mul).to(torch.bfloat16)
-    ok = (back == wt).numpy()
-    np.testing.assert_array_equal(got != 0xFF, ok)
-    np.testing.assert_array_equal(got[ok], qt.view(torch.uint8).numpy()[ok])
-    assert 0.3 < ok.mean() < 0.9
+    wv = wl.bf16_bits_to_f32(w).astype(np.float64)
+    scaled = np.ldexp(wv, 127 - c)                          # exact: a power of two
+    byte_of = {float(x): int(y) for x, y in zip(v, b) if x != 0}
+    want = np.full((N, K), 0xFF, np.uint8)
+    for idx in np.ndindex(N, K):
+        x = scaled[idx]
+        if x == 0:
+            want[idx] = 0x80 if np.signbit(x) else 0x00
+        elif x in byte_of:
+            want[idx] = byte_of[x]
+    np.testing.assert_array_equal(got, want)
+    assert 0.3 < (want != 0xFF).mean() < 0.9
 
 
 def test_from_dequant_refuses_nonfinite_and_bad_shapes():

@@ -9,7 +9,8 @@ lengths (the padding of a K % 128 tail sits past the valid prefix of the
 tile's last chunk and is not stored) -- and the weight pack is checked to be
 a permutation of the unpadded input (packed = standard[perm], the identity
 that vllm.models.deepseek_v41.common.ops.fused_layout builds its
-permutations on), the codes to carry padding code 128.
+permutations on), the codes to carry padding code 128, and the 16 bytes
+after the codes to hold the smallest and largest given code.
 """
 import numpy as np
 import pytest
@@ -43,15 +44,25 @@ def _ref_weights(elem, E, N, K, w):
     return np.ascontiguousarray(v[:, :tileb]).reshape(-1)
 
 
+def _trailer(codes):
+    """16 bytes after the packed codes: the smallest and the largest given
+    code, then zeros."""
+    t = np.zeros(16, np.uint8)
+    t[0], t[1] = codes.min(), codes.max()
+    return t
+
+
 def _ref_codes(layout, E, N, K, codes):
     Kp = -(-K // 128) * 128
     S, T = Kp // 128, N // 16
     Q = -(-S // 4)
     if layout == ROW32:
         v = _pad_cols(codes.reshape(E * N, K // 32), 16 * Q, 128).reshape(E, T, 16, Q, 4, 4)
-        return v.transpose(0, 1, 3, 5, 2, 4).reshape(-1)      # [e,t,q,j,r,u]
-    v = _pad_cols(codes.reshape(E * N // 32, K // 32), 16 * Q, 128).reshape(-1, Q, 4, 4)
-    return v.transpose(0, 1, 3, 2).reshape(-1)                # [R,q,j,u]
+        body = v.transpose(0, 1, 3, 5, 2, 4).reshape(-1)      # [e,t,q,j,r,u]
+    else:
+        v = _pad_cols(codes.reshape(E * N // 32, K // 32), 16 * Q, 128).reshape(-1, Q, 4, 4)
+        body = v.transpose(0, 1, 3, 2).reshape(-1)            # [R,q,j,u]
+    return np.concatenate([body, _trailer(codes)])
 
 
 SHAPES = [
@@ -136,7 +147,8 @@ def test_row32_code_pack_is_a_permutation_and_lane_dwords():
     src = np.zeros(n, np.int64)
     for p, plane in enumerate(_labels(n)):
         _, cp = oracle.pack_weights(E4M3, ROW32, E, N, K, w, plane.reshape(E * N, K // 32))
-        src |= cp.astype(np.int64) << (8 * p)
+        np.testing.assert_array_equal(cp[-16:], _trailer(plane))
+        src |= cp[:-16].astype(np.int64) << (8 * p)
     assert np.array_equal(np.sort(src), np.arange(n))
     # lane l's dword of quad q holds its row's codes of blocks 4 (4 q + u) + j
     rows, kc = np.divmod(src, K // 32)
@@ -159,17 +171,23 @@ def test_no_weight_padding_and_codes_128():
     assert Kp > K and wp.size == N * K            # the K tail stores no padding
     assert np.count_nonzero(wp == 0x11) == N * K
     S, Q = 13, 4
-    assert cp.size == (N // 16) * Q * 256
-    assert np.count_nonzero(cp == 7) == N * (K // 32)
-    assert np.count_nonzero(cp == 128) == cp.size - N * (K // 32)
+    assert cp.size == (N // 16) * Q * 256 + 16
+    body, trailer = cp[:-16], cp[-16:]
+    assert np.count_nonzero(body == 7) == N * (K // 32)
+    assert np.count_nonzero(body == 128) == body.size - N * (K // 32)
+    # the padding code 128 is not counted in the trailer's range
+    np.testing.assert_array_equal(trailer, [7, 7] + [0] * 14)
     wb, cb = oracle.packed_sizes(E4M3, BLK32, 1, 64, K)
     w2 = np.full((1, 64, K), 0x22, np.uint8)
     c2 = np.full((2, K // 32), 9, np.uint8)
+    c2[1, 5] = 0
+    c2[0, 48] = 254
     wp2, cp2 = oracle.pack_weights(E4M3, BLK32, 1, 64, K, w2, c2)
-    assert cp2.shape == (2 * Q * 16,)
+    assert cp2.shape == (2 * Q * 16 + 16,) and cb == cp2.size
     # 49 real blocks per 32-row group, the other 15 of the 4 quads are padding
-    assert np.count_nonzero(cp2 == 9) == 2 * (K // 32)
-    assert np.count_nonzero(cp2 == 128) == 2 * (16 * Q - K // 32)
+    assert np.count_nonzero(cp2[:-16] == 9) == 2 * (K // 32) - 2
+    assert np.count_nonzero(cp2[:-16] == 128) == 2 * (16 * Q - K // 32)
+    np.testing.assert_array_equal(cp2[-16:], [0, 254] + [0] * 14)
 
 
 def test_pack_rejects_bad_shapes():
