@@ -299,6 +299,24 @@ mx_status mx_moe_linear(int elem, int64_t E, int64_t N, int64_t K,
                         void *y, void *ws, size_t ws_bytes,
                         mx_stream_t stream);
 
+/* mx_moe_linear for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same product with the same kernels and results, but no workspace
+ * argument.  The combine's per-slot sums (T * topk * N fp32) go to a device
+ * buffer the library holds (4 MiB per GPU, kept until the process ends), so
+ * combine mode needs T * topk * N <= 1,048,576; per-slot mode uses no
+ * buffer.  The call allocates nothing.  Every call on one GPU shares that
+ * buffer: calls that overlap on one GPU (two streams, two threads) race and
+ * must be ordered by the caller.  The buffer's contents need no clearing
+ * (every value is written before it is read).
+ * Errors: as mx_moe_linear; MX_ERR_WORKSPACE when the combine would need
+ * more than 4 MiB (checked on the host before any device call). */
+mx_status mx_moe_linear_noalloc(int elem, int64_t E, int64_t N, int64_t K,
+                                const void *w_packed, const void *codes_packed,
+                                int64_t T, int64_t topk, const void *x, int64_t ldx,
+                                const int32_t *topk_ids, const float *topk_weights,
+                                void *y, mx_stream_t stream);
+
 /* ---- The MoE block around the grouped linear ---- */
 
 /* Load-time expert copies ([weights942] moe_copies).  Input, as a model's

@@ -69,6 +69,8 @@ def lib() -> C.CDLL:
         L.mx_moe_workspace.argtypes = [i32, i64, i64, i64, i64, i64, i32, C.POINTER(sz)]
         L.mx_moe_linear.argtypes = [i32, i64, i64, i64, p, p, i64, i64, p, i64, p, p, p,
                                     p, sz, p]
+        L.mx_moe_linear_noalloc.argtypes = [i32, i64, i64, i64, p, p, i64, i64, p, i64, p,
+                                            p, p, p]
         L.mx_moe_copies.argtypes = [i32, i64, i64, i64, i64, i64, p, p, p, p, p, p, p, p, p,
                                     sz, p]
         L.mx_moe_gate_up.argtypes = [i32, i64, i64, i64, p, p, i64, i64, p, i64, p, p, i64, p]
@@ -81,7 +83,8 @@ def lib() -> C.CDLL:
         L.mx_e4m3_from_dequant.argtypes = [i32, i64, i64, p, i64, p, p, p, sz, p]
         for name in ("mx_packed_sizes", "mx_pack_weights", "mx_quant_act", "mx_act_t16_sizes",
                      "mx_quant_act_t16", "mx_linear_workspace", "mx_linear", "mx_moe_workspace",
-                     "mx_moe_linear", "mx_moe_copies", "mx_moe_gate_up", "mx_moe_down",
+                     "mx_moe_linear", "mx_moe_linear_noalloc", "mx_moe_copies",
+                     "mx_moe_gate_up", "mx_moe_down",
                      "mx_fold_row_codes", "mx_e4m3_from_dequant", "mx_fused_layout_permute"):
             getattr(L, name).restype = i32
         _lib = L
@@ -174,6 +177,13 @@ def mx_moe_linear(elem, E, N, K, w_packed, codes_packed, T, topk, x, ldx, topk_i
     _check(lib().mx_moe_linear(elem, E, N, K, _ptr(w_packed), _ptr(codes_packed), T, topk,
                                _ptr(x), ldx, _ptr(topk_ids), _ptr(topk_weights), _ptr(y),
                                _ptr(ws), ws_bytes, _stream(stream)), "mx_moe_linear")
+
+
+def mx_moe_linear_noalloc(elem, E, N, K, w_packed, codes_packed, T, topk, x, ldx, topk_ids,
+                          topk_weights, y, stream=None):
+    _check(lib().mx_moe_linear_noalloc(elem, E, N, K, _ptr(w_packed), _ptr(codes_packed), T,
+                                       topk, _ptr(x), ldx, _ptr(topk_ids), _ptr(topk_weights),
+                                       _ptr(y), _stream(stream)), "mx_moe_linear_noalloc")
 
 
 def mx_moe_copies(elem, E, Np, inter, K, H, w13, s13, w2, s2, w13_out, s13_out, w2_out, s2_out,

@@ -499,6 +499,25 @@ mx_status mx_moe_linear(int elem, int64_t E, int64_t N, int64_t K, const void *w
                    topk_ids, topk_weights, y, N, ws, ws_bytes, stream);
 }
 
+mx_status mx_moe_linear_noalloc(int elem, int64_t E, int64_t N, int64_t K, const void *w_packed,
+                                const void *codes_packed, int64_t T, int64_t topk, const void *x,
+                                int64_t ldx, const int32_t *topk_ids, const float *topk_weights,
+                                void *y, mx_stream_t stream) {
+    size_t need = 0;
+    mx_status st = mx_moe_workspace(elem, E, N, K, T, topk, topk_weights ? 1 : 0, &need);
+    if (st != MX_OK) return st;
+    if (need > (size_t)mx::kStaticScratchBytes) return MX_ERR_WORKSPACE;   // beyond the buffer
+    // host-side checks first (moe_run repeats them), then the device's buffer
+    if (!w_packed || !codes_packed || !x || !topk_ids || !y) return MX_ERR_NULL;
+    void *ws = nullptr;
+    if (need > 0) {
+        if ((st = device_ok()) != MX_OK) return st;
+        if (!(ws = mx::static_scratch())) return MX_ERR_DEVICE;
+    }
+    return moe_run(elem, E, N, K, w_packed, codes_packed, T, topk, x, ldx, false, false,
+                   topk_ids, topk_weights, y, N, ws, need, stream);
+}
+
 mx_status mx_moe_copies(int elem, int64_t E, int64_t Np, int64_t inter, int64_t K, int64_t H,
                         const void *w13, const void *s13, const void *w2, const void *s2,
                         void *w13_out, void *s13_out, void *w2_out, void *s2_out, void *ws,

@@ -70,6 +70,12 @@ __host__ __device__ inline int64_t packed_code_body_bytes(int layout, int64_t E,
     return layout == 0 ? E * (N / 16) * Q * 256 : E * (N / 32) * Q * 16;
 }
 constexpr int64_t kCodeTrailer = 16;
+
+// The fixed device buffer of mx_moe_linear_noalloc (mx_static.hip): its size,
+// and the current device's address of it (looked up once per device;
+// nullptr if the lookup fails).
+constexpr int64_t kStaticScratchBytes = int64_t(4) << 20;
+void *static_scratch();
 // [weights942] moe_copies: the padding check (sets *bad), then the copies
 hipError_t launch_moe_padding_check(int elem, int64_t E, int64_t Np, int64_t inter, int64_t K,
                                     int64_t H, const void *w13, const void *w2, int *bad,

@@ -302,3 +302,24 @@ def test_fused_quant_kill_switch():
                          text=True, timeout=120, check=True).stdout
     t16 = 16 * 7168 + 16 * (7168 // 32)                # one 16-token tile of bytes and codes
     assert int(out.strip().splitlines()[-1]) >= t16
+
+
+def test_noalloc_moe_refuses_combine_beyond_its_buffer():
+    """mx_moe_linear_noalloc: the combine's per-slot sums must fit the
+    library's 4 MiB buffer (T * topk * N <= 2^20 fp32), checked on the host
+    before any device call; shape errors come first, as in mx_moe_linear."""
+    L = mx.lib()
+    f = C.c_float(1.0)
+    # 512 tokens x top-8 x 3072 outputs x 4 bytes = 48 MiB
+    assert L.mx_moe_linear_noalloc(1, 32, 3072, 3072, None, None, 512, 8, None, 3072, None,
+                                   C.byref(f), None, None) == WS
+    # exactly 2^20 floats would pass the size check (then fail on NULL pointers)
+    assert L.mx_moe_linear_noalloc(1, 32, 4096, 3072, None, None, 32, 8, None, 3072, None,
+                                   C.byref(f), None, None) == NULL
+    assert L.mx_moe_linear_noalloc(1, 32, 4096, 3072, None, None, 33, 8, None, 3072, None,
+                                   C.byref(f), None, None) == WS
+    # per-slot mode uses no buffer: only the NULL pointers are refused
+    assert L.mx_moe_linear_noalloc(1, 32, 3072, 3072, None, None, 512, 8, None, 3072, None,
+                                   None, None, None) == NULL
+    assert L.mx_moe_linear_noalloc(1, 32, 3072, 100, None, None, 16, 8, None, 3072, None,
+                                   None, None, None) == SHAPE
