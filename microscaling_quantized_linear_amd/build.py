@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmx.so")
 SOURCES = ["mx_pack.hip", "mx_ingest.hip", "mx_quant.hip", "mx_gemv.hip", "mx_gemv_w8.hip",
-           "mx_gemm.hip", "mx_static.hip", "mx_api.cpp"]
+           "mx_gemm.hip", "mx_static.hip", "mx_plan.cpp", "mx_api.cpp"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [

@@ -18,7 +18,9 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "mx_oracle.c")
-LIB = os.path.join(HERE, "libmx_oracle.so")
+# MX_ORACLE_LIB: another build of the same source (the sanitizer test runs the
+# oracle's pins on an AddressSanitizer / UBSan build this way)
+LIB = os.environ.get("MX_ORACLE_LIB") or os.path.join(HERE, "libmx_oracle.so")
 
 E4M3, E2M1 = 0, 1
 ROW32, BLK32 = 0, 1
@@ -28,13 +30,20 @@ ACT_BF16, ACT_MXFP8 = 0, 1
 _lib = None
 
 
-def build() -> str:
-    """Compile the oracle with gcc (-O2, no fast-math, OpenMP over rows)."""
-    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp", "-Wall",
-           "-o", LIB + ".tmp", SRC, "-lm"]
+def build(out: str | None = None, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, OpenMP over rows);
+    sanitize: an AddressSanitizer + UndefinedBehaviorSanitizer build (any
+    finding aborts) written to `out`."""
+    out = out or LIB
+    flags = ["-O2"]
+    if sanitize:
+        flags = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                 "-fno-sanitize-recover=all"]
+    cmd = ["gcc", *flags, "-std=c99", "-fPIC", "-shared", "-fopenmp", "-Wall",
+           "-o", out + ".tmp", SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 def lib() -> C.CDLL:
