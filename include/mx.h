@@ -265,6 +265,8 @@ mx_status mx_linear_workspace(int elem, int layout, int64_t N, int64_t K,
  *       (may be NULL when that is 0); its contents on return are unspecified
  * The call is asynchronous on `stream`, allocates nothing and may be
  * captured in a graph.
+ * Size limit: every buffer a kernel reads or writes (x, xq, y, the packed
+ * weights) must stay below 2 GiB (32-bit buffer offsets), else MX_ERR_SHAPE.
  * Built combinations: E4M3 x {ROW32, BLK32} x {BF16, MXFP8, MXFP8_T16};
  * E2M1 x ROW32 x BF16.  Others: MX_ERR_UNSUPPORTED. */
 mx_status mx_linear(int elem, int layout, int64_t N, int64_t K,

@@ -371,7 +371,7 @@ mx_status mx_linear(int elem, int layout, int64_t N, int64_t K, const void *w_pa
     if (need > 0 && (!ws || ws_bytes < need)) return MX_ERR_WORKSPACE;
     if (need > 0 && !aligned16(ws)) return MX_ERR_ALIGN;
     const bool gemm = use_gemm(act, M);
-    if (gemm && N * Kp > kMaxRsrc) return MX_ERR_SHAPE;
+    if (gemm && (N * Kp > kMaxRsrc || M * ldy * 2 > kMaxRsrc)) return MX_ERR_SHAPE;
     if ((st = device_ok()) != MX_OK) return st;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     uint8_t *wsp = static_cast<uint8_t *>(ws);

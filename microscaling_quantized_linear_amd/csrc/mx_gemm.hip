@@ -318,6 +318,20 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     auto pk = [](float lo, float hi) -> uint32_t {
         return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
     };
+    // Stores go through a buffer resource over y with 32-bit offsets worked
+    // out once per lane; an output past M or N gets an out-of-range offset and
+    // is dropped, so there is no branch and no 64-bit address per store (a
+    // branch per store also made the compiler reload the kernel arguments
+    // around each one).  The host keeps M * ldy * 2 below 2^31.
+    const __amdgpu_buffer_rsrc_t yr = make_rsrc(p.y, (uint32_t)(p.M * p.ldy * 2));
+    const uint32_t ldy2 = (uint32_t)p.ldy * 2u;
+    uint32_t ybase[2];                                    // token row of slab mt, or kOOB
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        const int64_t m = m0 + 64 * wave + 32 * mt + rr;
+        ybase[mt] = m < p.M ? (uint32_t)m * ldy2 + (uint32_t)(n0 + 8 * g) * 2u : kOOB;
+    }
+    const int64_t nlim = p.N - n0 - 8 * g;                // columns left for this lane's pieces
     auto epilogue = [&](auto biasconst) {
         constexpr bool kBias = decltype(biasconst)::value;
 #pragma unroll
@@ -331,7 +345,6 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
 #pragma unroll
             for (int mt = 0; mt < 2; ++mt) {
                 const v16f &c = acc[nt][mt];
-                const int64_t m = m0 + 64 * wave + 32 * mt + rr;
 #pragma unroll
                 for (int a0 = 0; a0 < 4; a0 += 2) {
                     uint32_t o[2][2];                     // [a - a0][dword]
@@ -355,10 +368,12 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
                         o[0][h] = sw[0];
                         o[1][h] = sw[1];
                     }
-                    const int64_t n = n0 + 32 * nt + 8 * (a0 + g);
-                    if (m < p.M && n < p.N)
-                        *reinterpret_cast<v4u *>(p.y + m * p.ldy + n) =
-                            v4u{o[0][0], o[0][1], o[1][0], o[1][1]};
+                    // columns n0 + 32 nt + 8 (a0 + g) .. + 7 (N % 16 == 0: all in or out)
+                    const uint32_t col = 32u * nt + 8u * a0;
+                    const uint32_t off = (int64_t)col < nlim ? ybase[mt] + 2u * col : kOOB;
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        v4u{o[0][0], o[0][1], o[1][0], o[1][1]}, yr, (int)(off | (off & kOOB)),
+                        0, 0);
                 }
             }
             // one tile at a time: reading every accumulator up front would

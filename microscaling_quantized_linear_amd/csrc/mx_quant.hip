@@ -84,40 +84,58 @@ __global__ void __launch_bounds__(256) quant_act_kernel(
 // Tokens past M, K past the end and blocks past K/32 read as byte 0 and code
 // 127, so every byte of both buffers is defined.
 //
-// One wavefront per 1 KB block (mb, s, h): lane (r, j) converts 16 values,
-// half of the 32-value block 4 s + 2 h + j / 2; the block maximum is taken
-// with the partner lane 16 apart (j xor 1).  Reads are 32 contiguous bytes per
-// lane; the write is the 1 KB block, contiguous.
+// One wavefront per (token tile mb, quad q of four steps): for each of the
+// quad's steps s and halves h, lane (r, j) converts 16 values, half of the
+// 32-value block 4 s + 2 h + j / 2 (the block maximum is taken with the
+// partner lane 16 apart, j xor 1), and the wavefront writes the 1 KB block
+// contiguously; then each lane writes its own code dword of the quad (token
+// r, block 4 (4 q + u) + j in byte u), gathered from the lanes that computed
+// those codes.  All of a lane's loads are issued before its first convert.
 template <int RULE>
 __global__ void __launch_bounds__(256) quant_act_t16_kernel(
     int64_t M, int64_t K, const uint16_t *__restrict__ x, int64_t ldx,
-    uint8_t *__restrict__ xq, uint8_t *__restrict__ xc, int64_t nblk) {
+    uint8_t *__restrict__ xq, uint8_t *__restrict__ xc, int64_t nunits) {
     const int64_t wid = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 64;
-    if (wid >= nblk) return;                         // whole wavefronts
+    if (wid >= nunits) return;                       // whole wavefronts
     const int lane = threadIdx.x % 64, r = lane % 16, j = lane / 16;
     const int64_t S = (K + 127) / 128, Q = (S + 3) / 4, KB = K / 32;
-    const int64_t h = wid % 2, s = (wid / 2) % S, mb = wid / (2 * S);
-    const int64_t m = 16 * mb + r, k0 = 128 * s + 64 * h + 16 * j;
-    const bool ok = m < M && k0 < K;                 // K % 32 == 0: 16 values all in or out
-    v4u v[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
-    if (ok) {
-        v[0] = *reinterpret_cast<const v4u *>(x + m * ldx + k0);
-        v[1] = *reinterpret_cast<const v4u *>(x + m * ldx + k0 + 8);
+    const int64_t q = wid % Q, mb = wid / Q;
+    const int64_t m = 16 * mb + r;
+    v4u v[4][2][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t k0 = 128 * (4 * q + u) + 64 * h + 16 * j;
+            // K % 32 == 0: the lane's 16 values are all inside K or all past it
+            const bool ok = m < M && k0 < K;
+            v[u][h][0] = ok ? *reinterpret_cast<const v4u *>(x + m * ldx + k0) : v4u{0u, 0u, 0u, 0u};
+            v[u][h][1] = ok ? *reinterpret_cast<const v4u *>(x + m * ldx + k0 + 8)
+                            : v4u{0u, 0u, 0u, 0u};
+        }
+    uint32_t code[4][2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t s = 4 * q + u;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const v4u o = quant_half_block<RULE>(v[u][h][0], v[u][h][1], code[u][h]);
+            if (s < S) *reinterpret_cast<v4u *>(xq + ((mb * S + s) * 2 + h) * 1024 + 16 * lane) = o;
+        }
     }
-    uint32_t code;
-    const v4u o = quant_half_block<RULE>(v[0], v[1], code);
-    *reinterpret_cast<v4u *>(xq + ((mb * S + s) * 2 + h) * 1024 + 16 * lane) = o;
-    // the even lane of each pair writes the block's code
-    if (j % 2 == 0) {
-        const int64_t blk = 4 * s + 2 * h + j / 2;
-        const uint32_t c = (m < M && blk < KB) ? code : 127u;
-        xc[(mb * Q + s / 4) * 256 + 4 * (16 * (blk % 4) + r) + s % 4] = (uint8_t)c;
+    // lane (r, j) owns block 4 s + j of each step: half j / 2, computed by
+    // the lanes 16 (2 (j % 2)) + r and 16 (2 (j % 2) + 1) + r of that half
+    const int src = 32 * (j % 2) + r;
+    uint32_t dw = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t c0 = (uint32_t)__shfl((int)code[u][0], src);
+        const uint32_t c1 = (uint32_t)__shfl((int)code[u][1], src);
+        const int64_t blk = 4 * (4 * q + u) + j;
+        const uint32_t c = (m < M && blk < KB) ? (j / 2 ? c1 : c0) : 127u;
+        dw |= c << (8 * u);
     }
-    // steps 4 Q - 1 .. S are never visited: their code bytes are padding
-    if (h == 0 && s == S - 1 && j % 2 == 0)
-        for (int64_t s2 = S; s2 < 4 * Q; ++s2)
-            for (int jb = j / 2; jb < 4; jb += 2)
-                xc[(mb * Q + s2 / 4) * 256 + 4 * (16 * jb + r) + s2 % 4] = 127u;
+    reinterpret_cast<uint32_t *>(xc)[(mb * Q + q) * 64 + lane] = dw;
 }
 
 hipError_t launch_quant(int64_t M, int64_t K, const void *x, int64_t ldx, void *xq, int64_t ldq,
@@ -135,14 +153,14 @@ hipError_t launch_quant(int64_t M, int64_t K, const void *x, int64_t ldx, void *
 
 hipError_t launch_quant_t16(int64_t M, int64_t K, const void *x, int64_t ldx, void *xq,
                             void *xc, int rule, hipStream_t stream) {
-    const int64_t S = (K + 127) / 128, nblk = (M + 15) / 16 * S * 2;
-    const dim3 grid((unsigned)((nblk + 3) / 4)), block(256);
+    const int64_t S = (K + 127) / 128, Q = (S + 3) / 4, nunits = (M + 15) / 16 * Q;
+    const dim3 grid((unsigned)((nunits + 3) / 4)), block(256);
     if (rule == RULE_OCP)
         hipLaunchKernelGGL(quant_act_t16_kernel<RULE_OCP>, grid, block, 0, stream, M, K,
-                           (const uint16_t *)x, ldx, (uint8_t *)xq, (uint8_t *)xc, nblk);
+                           (const uint16_t *)x, ldx, (uint8_t *)xq, (uint8_t *)xc, nunits);
     else
         hipLaunchKernelGGL(quant_act_t16_kernel<RULE_CEIL448>, grid, block, 0, stream, M, K,
-                           (const uint16_t *)x, ldx, (uint8_t *)xq, (uint8_t *)xc, nblk);
+                           (const uint16_t *)x, ldx, (uint8_t *)xq, (uint8_t *)xc, nunits);
     return hipGetLastError();
 }
 
