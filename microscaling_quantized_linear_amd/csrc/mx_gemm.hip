@@ -41,8 +41,9 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // TAIL: K % 128 != 0, the last step's chunks are cut to their valid prefix
 // (instantiated apart so the steady-state copies of whole-step shapes carry
-// no extra mask)
-template <int LAYOUT, int NTW, bool TAIL>
+// no extra mask).  REM: the step count S is not a multiple of eight, so the
+// last iteration of the eight-step loop stops after step S - 1.
+template <int LAYOUT, int NTW, bool TAIL, bool REM>
 __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     constexpr int BN = NTW * 32;
     constexpr int kWBytes = 2 * NTW * 2048;               // one step's weight chunks
@@ -287,8 +288,9 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
     issue(lds0, 1, 1);
     // eight steps (two quads) per iteration: each LDS buffer and activation
     // register set is a fixed object and the two scale sets alternate without
-    // copies; a step at or past S reads zeros and adds nothing
-    for (int s = 0; s < S; s += 8) {
+    // copies
+    const int S8 = REM ? S / 8 * 8 : S;
+    for (int s = 0; s < S8; s += 8) {
         const int q = s / 4;
         load_qscales(q + 1, qb);
         if (s == 0)
@@ -303,6 +305,38 @@ __global__ void __launch_bounds__(256, 1) gemm_w8a8_kernel(GemmArgs p) {
         step(lds1, lds2, lds3, s + 5, qb, bb, ba, U1{}, F0{}, P2{});
         step(lds2, lds3, lds0, s + 6, qb, ba, bb, U2{}, F0{}, P0{});
         step(lds3, lds0, lds1, s + 7, qb, bb, ba, U3{}, F0{}, P2{});
+    }
+    // REM: the last S % 8 steps, the leading steps of one more iteration in
+    // nested uniform conditions (every wavefront takes the same ones, with
+    // their barriers; loads issued for the steps not taken read zeros).
+    // With S < 8 the loop did not run and the accumulators start at zero.
+    if (REM && S8 < S) {
+        const int s = S8, q = s / 4;
+        if (s == 0) {
+#pragma unroll
+            for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt) acc[nt][mt] = v16f{};
+        }
+        load_qscales(q + 1, qb);
+        step(lds0, lds1, lds2, s + 0, qa, ba, bb, U0{}, F0{}, P0{});
+        if (s + 1 < S) {
+            step(lds1, lds2, lds3, s + 1, qa, bb, ba, U1{}, F0{}, P2{});
+            if (s + 2 < S) {
+                step(lds2, lds3, lds0, s + 2, qa, ba, bb, U2{}, F0{}, P0{});
+                if (s + 3 < S) {
+                    step(lds3, lds0, lds1, s + 3, qa, bb, ba, U3{}, F0{}, P2{});
+                    if (s + 4 < S) {
+                        step(lds0, lds1, lds2, s + 4, qb, ba, bb, U0{}, F0{}, P0{});
+                        if (s + 5 < S) {
+                            step(lds1, lds2, lds3, s + 5, qb, bb, ba, U1{}, F0{}, P2{});
+                            if (s + 6 < S)
+                                step(lds2, lds3, lds0, s + 6, qb, ba, bb, U2{}, F0{}, P0{});
+                        }
+                    }
+                }
+            }
+        }
     }
 
     // ---- epilogue, straight from registers: element i of lane (g, rr) in
@@ -391,12 +425,14 @@ template <int LAYOUT, int NTW>
 static hipError_t launch_ntw(const GemmArgs &a, hipStream_t st) {
     constexpr int BN = NTW * 32;
     const int64_t tiles = ((a.N + BN - 1) / BN) * ((a.M + kBM - 1) / kBM);
-    if (a.K % 128 != 0)
-        hipLaunchKernelGGL((gemm_w8a8_kernel<LAYOUT, NTW, true>), dim3((unsigned)tiles),
-                           dim3(256), 0, st, a);
+    const dim3 grid((unsigned)tiles), block(256);
+    const bool tail = a.K % 128 != 0, rem = (a.K + 127) / 128 % 8 != 0;
+    if (tail)
+        hipLaunchKernelGGL((gemm_w8a8_kernel<LAYOUT, NTW, true, true>), grid, block, 0, st, a);
+    else if (rem)
+        hipLaunchKernelGGL((gemm_w8a8_kernel<LAYOUT, NTW, false, true>), grid, block, 0, st, a);
     else
-        hipLaunchKernelGGL((gemm_w8a8_kernel<LAYOUT, NTW, false>), dim3((unsigned)tiles),
-                           dim3(256), 0, st, a);
+        hipLaunchKernelGGL((gemm_w8a8_kernel<LAYOUT, NTW, false, false>), grid, block, 0, st, a);
     return hipGetLastError();
 }
 

@@ -167,6 +167,21 @@ def test_gemm_small(g, layout, M, N, K):
     assert np.array_equal(y, y2)
 
 
+@pytest.mark.parametrize("K", [96, 640, 928, 1152, 1184, 1280, 1408, 1536, 1664, 1792, 1920, 2048])
+def test_gemm_step_remainders(g, K):
+    """The GEMM's K loop runs eight 128-K steps an iteration and then the
+    S % 8 steps left (S = ceil(K / 128)): every remainder 0 .. 7, with and
+    without a partial last step, with fewer than eight steps and with more."""
+    M, N = 80, 64
+    for layout in (ROW32, BLK32):
+        w, codes, x, bias = _dense_inputs([46, M, N, K, layout], E4M3, layout, M, N, K)
+        wp, cp = g.pack(E4M3, layout, 1, N, K, w, codes)
+        oq, oc = oracle.quant_act(x, OCP)
+        ref = oracle.linear(E4M3, layout, N, K, w, codes, M, MXFP8, xq=oq, xcodes=oc, bias=bias)
+        y = g.linear(E4M3, layout, N, K, wp, cp, MXFP8, x=x, rule=OCP, bias=bias)
+        g.assert_close(y, ref, f"gemm K={K} layout={layout}")
+
+
 def test_extreme_codes_w8a8(g):
     # weight codes 0, 1 and 254 with activations scaled by 2^-100, so that the
     # results stay inside bf16's range; activation codes near 19
