@@ -50,3 +50,42 @@ def test_noalloc_moe_matches_workspace_path_twice(g):
             assert np.array_equal(y_ws, y_na), f"noalloc differs from the workspace path: {c}"
             ref = oracle.moe_linear(1, E, N, K, d["w"], d["codes"], d["x"], d["ids"], wts)
             g.assert_close(y_na, ref, f"noalloc {c}")
+
+
+def test_noalloc_moe_graph_replays(g):
+    """The callers it is for capture it in a HIP graph: every replay gives the
+    eager result bit for bit, also when an eager call with another input used
+    the library's buffer in between (calls ordered on one stream)."""
+    import torch
+    import microscaling_quantized_linear_amd as mx
+    a = wl.moe_inputs(4, E=8, N=256, K=512, T=6, topk=3, seed=2)
+    b = wl.moe_inputs(4, E=8, N=256, K=512, T=9, topk=2, seed=3)
+    E, N, K = 8, 256, 512
+    wp, cp = g.pack(1, 0, E, N, K, a["w"], a["codes"])
+    x, ids, wts = g.dev(a["x"]), g.dev(a["ids"]), g.dev(a["weights"])
+    xb, idsb, wtsb = g.dev(b["x"]), g.dev(b["ids"]), g.dev(b["weights"])
+    y = torch.empty((6, N), dtype=torch.int16, device=g.DEV)
+    yb = torch.empty((9, N), dtype=torch.int16, device=g.DEV)
+
+    def run():
+        mx.mx_moe_linear_noalloc(1, E, N, K, wp, cp, 6, 3, x, K, ids, wts, y)
+
+    def other():
+        mx.mx_moe_linear_noalloc(1, E, N, K, wp, cp, 9, 2, xb, K, idsb, wtsb, yb)
+
+    run()
+    torch.cuda.synchronize()
+    ref = y.clone()
+    ref_np = g.host_u16(y)
+    g.assert_close(ref_np, oracle.moe_linear(1, E, N, K, a["w"], a["codes"], a["x"], a["ids"],
+                                             a["weights"]), "noalloc eager")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, capture_error_mode="thread_local"):
+        run()
+    for _ in range(4):
+        y.zero_()
+        other()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), "a replay differs from the eager call"
