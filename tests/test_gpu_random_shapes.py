@@ -1,0 +1,113 @@
+"""Parity against the oracle over seeded random shapes and options.
+
+The hand-picked cases in test_gpu_parity.py fix the workloads, the tile and
+step boundaries and the edge cases; these add breadth: random M (decode GEMV
+and prefill GEMM sides), N, K (ragged 128-K steps included), both weight
+formats and code layouts, every activation form, bias on or off, and grouped
+MoE launches with random expert counts, routing and top-k, per slot and
+combined.  The case list is drawn once from a fixed seed, so every run checks
+the same cases and a failure names its case."""
+import numpy as np
+import pytest
+
+import oracle
+from microscaling_quantized_linear_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+E4M3, E2M1, ROW32, BLK32 = 0, 1, 0, 1
+BF16, MXFP8, MXFP8_T16, OCP, CEIL = 0, 1, 2, 0, 1
+
+
+@pytest.fixture(scope="module")
+def g():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mxgpu
+    return mxgpu
+
+
+def _dense_cases(n=100):
+    rng = np.random.default_rng(20261202)
+    out = []
+    for i in range(n):
+        elem = E2M1 if rng.random() < 0.25 else E4M3
+        layout = ROW32 if elem == E2M1 or rng.random() < 0.5 else BLK32
+        if elem == E2M1:
+            act = BF16
+        else:
+            act = [BF16, MXFP8, MXFP8, MXFP8_T16][rng.integers(0, 4)]
+        # decode side (M <= 16, sometimes up to 64) or prefill side (M > 64)
+        M = int(rng.choice([rng.integers(1, 17), rng.integers(17, 65), rng.integers(65, 300)],
+                           p=[0.5, 0.2, 0.3]))
+        N = int(32 * rng.integers(1, 25)) if layout == BLK32 else int(16 * rng.integers(1, 49))
+        K = int(32 * rng.integers(1, 97))
+        prequant = act == MXFP8 and rng.random() < 0.4
+        rule = OCP if rng.random() < 0.7 else CEIL
+        bias = rng.random() < 0.5
+        out.append(dict(i=i, elem=elem, layout=layout, act=act, M=M, N=N, K=K,
+                        prequant=bool(prequant), rule=rule, bias=bool(bias)))
+    return out
+
+
+def _moe_cases(n=40):
+    rng = np.random.default_rng(20261203)
+    out = []
+    for i in range(n):
+        E = int(rng.integers(1, 13))
+        topk = int(rng.integers(1, min(E, 4) + 1))
+        out.append(dict(i=i, elem=E2M1 if rng.random() < 0.7 else E4M3, E=E, topk=topk,
+                        T=int(rng.integers(1, 41)), N=int(16 * rng.integers(1, 17)),
+                        K=int(32 * rng.integers(1, 41)), combine=bool(rng.random() < 0.5)))
+    return out
+
+
+DENSE = _dense_cases()
+MOE = _moe_cases()
+
+
+@pytest.mark.parametrize("c", DENSE, ids=lambda c: "dense{i}_e{elem}l{layout}a{act}_M{M}N{N}K{K}".format(**c))
+def test_random_dense(g, c):
+    elem, layout, act, M, N, K = c["elem"], c["layout"], c["act"], c["M"], c["N"], c["K"]
+    rng = np.random.default_rng([31, c["i"]])
+    w = wl.e4m3_bytes(rng, (N, K)) if elem == E4M3 else wl.fp4_bytes(rng, (N, K // 2))
+    codes = wl.codes(rng, (N, K // 32) if layout == ROW32 else (N // 32, K // 32), 112, 140)
+    x = wl.activations(rng, (M, K), 0.01)
+    bias = wl.activations(rng, (N,)) if c["bias"] else None
+    wp, cp = g.pack(elem, layout, 1, N, K, w, codes)
+    what = f"case {c}"
+    if act == BF16:
+        ref = oracle.linear(elem, layout, N, K, w, codes, M, BF16, x=x, bias=bias)
+        y = g.linear(elem, layout, N, K, wp, cp, BF16, x=x, bias=bias)
+    else:
+        oq, oc = oracle.quant_act(x, c["rule"])
+        ref = oracle.linear(elem, layout, N, K, w, codes, M, MXFP8, xq=oq, xcodes=oc, bias=bias)
+        if act == MXFP8_T16:
+            if -(-K // 128) > 64 and M <= 64:
+                pytest.skip("T16 input beyond the decode GEMV's 64 steps is refused by design")
+            xqd, xcd = g.quant_t16(x, c["rule"])
+            y = g.linear(elem, layout, N, K, wp, cp, MXFP8_T16, xq=xqd, xcodes=xcd, bias=bias, M=M)
+        elif c["prequant"]:
+            y = g.linear(elem, layout, N, K, wp, cp, MXFP8, xq=oq, xcodes=oc, bias=bias)
+        else:
+            y = g.linear(elem, layout, N, K, wp, cp, MXFP8, x=x, rule=c["rule"], bias=bias)
+    g.assert_close(y, ref, what)
+
+
+@pytest.mark.parametrize("c", MOE, ids=lambda c: "moe{i}_e{elem}_E{E}T{T}k{topk}N{N}K{K}c{combine}".format(**c))
+def test_random_moe(g, c):
+    elem, E, T, topk, N, K = c["elem"], c["E"], c["T"], c["topk"], c["N"], c["K"]
+    rng = np.random.default_rng([32, c["i"]])
+    w = wl.fp4_bytes(rng, (E, N, K // 2)) if elem == E2M1 else wl.e4m3_bytes(rng, (E, N, K))
+    codes = wl.codes(rng, (E * N, K // 32), 112, 140)
+    x = wl.activations(rng, (T, K))
+    # distinct experts per token; now and then an out-of-range id (a zero row)
+    ids = np.stack([rng.permutation(E)[:topk] for _ in range(T)]).astype(np.int32)
+    if rng.random() < 0.3:
+        ids[rng.integers(0, T), rng.integers(0, topk)] = E + 3
+    weights = rng.random((T, topk)).astype(np.float32) if c["combine"] else None
+    wp, cp = g.pack(elem, ROW32, E, N, K, w, codes)
+    ref = oracle.moe_linear(elem, E, N, K, w, codes, x, ids, weights)
+    y = g.moe(elem, E, N, K, wp, cp, x, ids, weights)
+    g.assert_close(y, ref, f"case {c}")
