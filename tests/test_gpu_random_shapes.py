@@ -111,3 +111,44 @@ def test_random_moe(g, c):
     ref = oracle.moe_linear(elem, E, N, K, w, codes, x, ids, weights)
     y = g.moe(elem, E, N, K, wp, cp, x, ids, weights)
     g.assert_close(y, ref, f"case {c}")
+
+
+def _block_cases(n=12):
+    rng = np.random.default_rng(20261204)
+    out = []
+    for i in range(n):
+        E = int(rng.integers(1, 9))
+        out.append(dict(i=i, elem=E2M1 if rng.random() < 0.7 else E4M3, E=E,
+                        topk=int(rng.integers(1, min(E, 4) + 1)), T=int(rng.integers(1, 25)),
+                        inter=int(32 * rng.integers(1, 13)), H=int(32 * rng.integers(1, 13))))
+    return out
+
+
+@pytest.mark.parametrize("c", _block_cases(),
+                         ids=lambda c: "block{i}_e{elem}_E{E}T{T}k{topk}I{inter}H{H}".format(**c))
+def test_random_moe_block(g, c):
+    """mx_moe_gate_up (interleaved gate/up rows, silu(gate) * up) and
+    mx_moe_down (one hidden row per slot, per slot and combined) at random
+    shapes, against the oracle."""
+    elem, E, T, topk, inter, H = c["elem"], c["E"], c["T"], c["topk"], c["inter"], c["H"]
+    rng = np.random.default_rng([33, c["i"]])
+    rb = (lambda n: n // 2) if elem == E2M1 else (lambda n: n)
+    draw = wl.fp4_bytes if elem == E2M1 else wl.e4m3_bytes
+    w13 = draw(rng, (E, 2 * inter, rb(H)))
+    s13 = wl.codes(rng, (E * 2 * inter, H // 32), 112, 140)
+    w2 = draw(rng, (E, H, rb(inter)))
+    s2 = wl.codes(rng, (E * H, inter // 32), 112, 140)
+    x = wl.activations(rng, (T, H))
+    ids = np.stack([rng.permutation(E)[:topk] for _ in range(T)]).astype(np.int32)
+    wts = rng.random((T, topk)).astype(np.float32)
+    wp13, cp13 = g.pack(elem, ROW32, E, 2 * inter, H, w13, s13)
+    wp2, cp2 = g.pack(elem, ROW32, E, H, inter, w2, s2)
+    href = oracle.moe_gate_up(elem, E, inter, H, w13, s13, x, ids)
+    h = g.moe_gate_up(elem, E, inter, H, wp13, cp13, x, ids)
+    g.assert_close(h.reshape(T, topk, inter), href, f"gate_up {c}")
+    a = wl.activations(rng, (T * topk, inter))
+    g.assert_close(g.moe_down(elem, E, H, inter, wp2, cp2, a, ids).reshape(T, topk, H),
+                   oracle.moe_linear_rows(elem, E, H, inter, w2, s2, a, ids), f"down {c}")
+    g.assert_close(g.moe_down(elem, E, H, inter, wp2, cp2, a, ids, wts).reshape(T, H),
+                   oracle.moe_linear_rows(elem, E, H, inter, w2, s2, a, ids, wts),
+                   f"down combined {c}")
