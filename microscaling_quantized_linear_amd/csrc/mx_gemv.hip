@@ -145,7 +145,15 @@ gemv_kernel(GemvArgs p) {
     const __amdgpu_buffer_rsrc_t xcr =
         make_rsrc(p.xcodes, ACT == ACT_MXFP8 ? (uint32_t)(p.xrows * p.ldc) : 0u);
 
-    const int64_t s0 = (wave * S) / NW, s1 = ((wave + 1) * S) / NW;
+    // Grouped A16 with chunks of two steps: wavefront ranges start on even
+    // steps, so both steps of a chunk lie in one quad and share its code
+    // dwords (loaded once a chunk instead of once a step).  Four or more
+    // wavefronts only: with two (the K = 1536 down projection) the kernel
+    // then spills a few registers and runs slower.
+    constexpr bool kPairCodes = MOE && ACT == ACT_BF16 && P == 2 && NW >= 4;
+    const int64_t b0 = (wave * S) / NW, b1 = ((wave + 1) * S) / NW;
+    const int64_t s0 = kPairCodes ? (b0 & ~int64_t(1)) : b0;
+    const int64_t s1 = kPairCodes && wave + 1 < NW ? (b1 & ~int64_t(1)) : b1;
 
     // A16: is any weight code outside kLo .. kHi?  The register-tight grouped
     // A16W4 GEMV reads the tensor's code range from the packed codes' trailer
@@ -181,7 +189,7 @@ gemv_kernel(GemvArgs p) {
 
     // A16 weights and codes of step s (out of range beyond s1), requested
     // before the step's activations
-    auto loadw = [&](int64_t s) {
+    auto loadw = [&](int64_t s, bool codes = true) {
         StepA16<G> st;
         const bool in = s < s1;
 #pragma unroll
@@ -189,6 +197,7 @@ gemv_kernel(GemvArgs p) {
             st.a0[g] = load16<kNT>(wr, woff(g, s, in, 0));
             if (ELEM == E4M3) st.a1[g] = load16<kNT>(wr, woff(g, s, in, 1));
         }
+        if (!codes) return st;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             if (ELEM == E4M3) {
@@ -327,8 +336,8 @@ gemv_kernel(GemvArgs p) {
                     st.x3 = load16(xr, v0 ? xbase + (uint32_t)(2 * k0 + 48) : kOOB);
                 }
             };
-            auto load = [&](int64_t s) {
-                StepA16<G> st = loadw(s);
+            auto load = [&](int64_t s, bool codes = true) {
+                StepA16<G> st = loadw(s, codes);
                 loadx(st, s);
                 return st;
             };
@@ -376,7 +385,19 @@ gemv_kernel(GemvArgs p) {
             for (int64_t c = s0; c < s1; c += P) {
                 StepA16<G> st[P];
 #pragma unroll
-                for (int u = 0; u < P; ++u) st[u] = load(c + u);
+                for (int u = 0; u < P; ++u) {
+                    if (kPairCodes && u == 1) {
+                        // c is even: step c + 1 is in step c's quad
+                        st[1] = load(c + 1, false);
+#pragma unroll
+                        for (int g = 0; g < G; ++g) {
+                            st[1].cw[g] = st[0].cw[g];
+                            st[1].cw2[g] = st[0].cw2[g];
+                        }
+                    } else {
+                        st[u] = load(c + u);
+                    }
+                }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int u = 0; u < P; ++u) compute(st[u], c + u);
