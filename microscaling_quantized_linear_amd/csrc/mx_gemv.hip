@@ -106,9 +106,12 @@ __device__ inline v4f a16_exact_tile(v4f acc, v4u a0, v4u a1, v4u x0, v4u x1,
 // with chunks of two steps the kernel fits the register budget of four
 // wavefronts per SIMD without spilling, which keeps them all resident at once
 // (measured on MI355X: 29.8-30.3 against 32.1-33.3 us at E = 32, N = K = 3072).
+// With NW = 2 (the K = 1536 down projection) three wavefronts per SIMD keep
+// its ~1,500 workgroups resident too, and leave the registers that sharing
+// the code dwords of a chunk needs (47.2 against 48.1 us for the MoE block).
 template <int ELEM, int LAYOUT, int ACT, bool MOE, int NW, int P, int G>
 __global__ void __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(MOE && ELEM == E2M1 && P <= 2 ? 4 : 1)))
+__attribute__((amdgpu_waves_per_eu(MOE && ELEM == E2M1 && P <= 2 ? (NW >= 4 ? 4 : 3) : 1)))
 gemv_kernel(GemvArgs p) {
     const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
     const int r = lane % 16, j = lane / 16;
@@ -147,10 +150,8 @@ gemv_kernel(GemvArgs p) {
 
     // Grouped A16 with chunks of two steps: wavefront ranges start on even
     // steps, so both steps of a chunk lie in one quad and share its code
-    // dwords (loaded once a chunk instead of once a step).  Four or more
-    // wavefronts only: with two (the K = 1536 down projection) the kernel
-    // then spills a few registers and runs slower.
-    constexpr bool kPairCodes = MOE && ACT == ACT_BF16 && P == 2 && NW >= 4;
+    // dwords (loaded once a chunk instead of once a step).
+    constexpr bool kPairCodes = MOE && ACT == ACT_BF16 && P == 2 && NW >= 2;
     const int64_t b0 = (wave * S) / NW, b1 = ((wave + 1) * S) / NW;
     const int64_t s0 = kPairCodes ? (b0 & ~int64_t(1)) : b0;
     const int64_t s1 = kPairCodes && wave + 1 < NW ? (b1 & ~int64_t(1)) : b1;
