@@ -114,9 +114,13 @@ int env_choice(const char *name) {
 // Launch shape of the GEMV (see mx_kernels.h).  MX_GEMV_WAVES, MX_GEMV_CHUNK
 // and MX_GEMV_TILES override it (tuning sweeps only; read once).
 // Defaults measured on MI355X with graph-replayed launches: long K (S >= 32
-// steps, e.g. 7168) 8 waves x chunks of 4 steps x 2 tiles; shorter K 4 waves
-// x 4 steps x 1 tile; grouped MoE 2 steps x 4 tiles of an expert, 4 waves from
-// 16 steps (K >= 2048), else 2 (K = 1536 down projection: 17.7 vs 21.0 us).
+// steps, e.g. 7168) 8 waves x chunks of 4 steps x 2 tiles; 16 <= S < 32 4
+// waves x 4 steps x 1 tile; 8 <= S < 16 2 waves x 8 steps (every step of a
+// wavefront in one chunk: M = 8, N = 4096, K = 1568 3.93 against 4.04 us
+// with 4 waves x 4 steps); S < 8 2 waves x 2 steps (M = 1, N = 256, K = 512:
+// 2.52 against 2.65 us with chunks of 4); grouped MoE 2 steps x 4 tiles of
+// an expert, 4 waves from 16 steps (K >= 2048), else 2 (K = 1536 down
+// projection: 17.7 vs 21.0 us).
 mx::GemvShape gemv_shape(int64_t S, bool moe) {
     static const int f_nw = env_choice("MX_GEMV_WAVES"), f_chunk = env_choice("MX_GEMV_CHUNK"),
                      f_tiles = env_choice("MX_GEMV_TILES");
@@ -125,8 +129,12 @@ mx::GemvShape gemv_shape(int64_t S, bool moe) {
         g = {S >= 16 ? 4 : S >= 2 ? 2 : 1, 2, 4};
     else if (S >= 32)
         g = {8, 4, 2};
+    else if (S >= 16)
+        g = {4, 4, 1};
+    else if (S >= 8)
+        g = {2, 8, 1};
     else
-        g = {S >= 8 ? 4 : S >= 2 ? 2 : 1, 4, 1};
+        g = {S >= 2 ? 2 : 1, 2, 1};
     if (f_nw) g.nw = f_nw;
     if (f_chunk) g.chunk = f_chunk < 2 ? 2 : f_chunk;
     if (f_tiles) g.tiles = f_tiles > 4 ? 4 : f_tiles;
