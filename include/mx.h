@@ -391,7 +391,11 @@ mx_status mx_moe_down(int elem, int64_t E, int64_t H, int64_t inter,
  * setting (0 or 1). */
 int mx_set_batch_invariant(int on);
 
-/* Static description of a status code (never NULL). */
+/* Static description of a status code (never NULL).
+ * Dispatch trace: with the environment variable MX_LOG=1 (read once per
+ * process) mx_linear and the MoE entry points write one line to stderr for
+ * every kernel they launch, naming the kernel, its launch plan and the
+ * shape. */
 const char *mx_status_str(mx_status status);
 
 /* Whether an architecture name (e.g. "gfx950:sramecc+:xnack-") is one the

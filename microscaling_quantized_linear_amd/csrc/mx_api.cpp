@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdarg>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 
@@ -105,6 +107,29 @@ mx_status device_ok() {
 
 mx_status launched(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_LAUNCH; }
 
+// Dispatch trace: with MX_LOG=1 in the environment (read once per process)
+// every launch decision of the hot path goes to stderr as one line: entry
+// point, kernel and its launch plan, and the shape.  Off by default; no
+// output and no cost beyond one branch otherwise.
+bool log_on() {
+    static const bool on = [] {
+        const char *s = std::getenv("MX_LOG");
+        return s && s[0] && s[0] != '0';
+    }();
+    return on;
+}
+__attribute__((format(printf, 1, 2))) void log_dispatch(const char *fmt, ...) {
+    if (!log_on()) return;
+    char buf[256];
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    std::fprintf(stderr, "mx: %s\n", buf);
+}
+const char *layout_name(int layout) { return layout == ROW32 ? "ROW32" : "BLK32"; }
+const char *elem_name(int elem) { return elem == E4M3 ? "E4M3" : "E2M1"; }
+
 int env_choice(const char *name) {
     const char *s = std::getenv(name);
     const int v = s ? std::atoi(s) : 0;
@@ -182,11 +207,19 @@ mx_status moe_run(int elem, int64_t E, int64_t N, int64_t K, const void *w_packe
     a.epi = epi ? 1 : 0;
     float *slots = topk_weights ? static_cast<float *>(ws) : nullptr;
     a.ws = slots;
-    if ((st = launched(mx::launch_gemv(elem, ROW32, ACT_BF16, true, a,
-                                       gemv_shape(Kp / 128, true), s))) != MX_OK)
+    const mx::GemvShape sh = gemv_shape(Kp / 128, true);
+    log_dispatch("moe %s%s%s: gemv_kernel A16%s grouped, %d waves x %d-step chunks x %d tiles; "
+                 "E=%lld N=%lld K=%lld T=%lld topk=%lld",
+                 xslot ? "xslot " : "", epi ? "silu " : "", topk_weights ? "combined" : "per-slot",
+                 elem == E4M3 ? "W8" : "W4", sh.nw, sh.chunk, sh.tiles, (long long)E,
+                 (long long)N, (long long)K, (long long)T, (long long)topk);
+    if ((st = launched(mx::launch_gemv(elem, ROW32, ACT_BF16, true, a, sh, s))) != MX_OK)
         return st;
-    if (topk_weights)
+    if (topk_weights) {
+        log_dispatch("moe: moe_combine_kernel T=%lld topk=%lld N=%lld", (long long)T,
+                     (long long)topk, (long long)N);
         return launched(mx::launch_moe_combine(T, topk, N, slots, topk_weights, y, s));
+    }
     return MX_OK;
 }
 
@@ -402,6 +435,10 @@ mx_status mx_linear(int elem, int layout, int64_t N, int64_t K, const void *w_pa
         g.bias = static_cast<const uint16_t *>(bias);
         g.y = static_cast<uint16_t *>(y);
         g.ldy = ldy;
+        log_dispatch("linear: gemv_w8_fused_kernel %s, quantization inside (rule %d), "
+                     "%d waves x %d steps x %d tiles; M=%lld N=%lld K=%lld",
+                     layout_name(layout), rule, w8.nw, w8.spw, w8.g, (long long)M, (long long)N,
+                     (long long)K);
         return launched(mx::launch_gemv_w8_fused(layout, rule, g, w8, s));
     }
     if (incall && !gemm && !w8.ok) {
@@ -410,12 +447,16 @@ mx_status mx_linear(int elem, int layout, int64_t N, int64_t K, const void *w_pa
         uint8_t *q = wsp, *c = wsp + round256(M * Kp);
         lq = Kp;
         lc = Kp / 32;
+        log_dispatch("linear: quant_act_kernel (row-major, rule %d) M=%lld K=%lld", rule,
+                     (long long)M, (long long)K);
         if ((st = launched(mx::launch_quant(M, K, x, ldx, q, lq, c, lc, rule, s))) != MX_OK)
             return st;
         aq = q;
         ac = c;
     } else if (incall) {
         uint8_t *q = wsp, *c = wsp + round256(mx::act_t16_data_bytes(M, K));
+        log_dispatch("linear: quant_act_t16_kernel (rule %d) M=%lld K=%lld", rule, (long long)M,
+                     (long long)K);
         if ((st = launched(mx::launch_quant_t16(M, K, x, ldx, q, c, rule, s))) != MX_OK) return st;
         aq = q;
         ac = c;
@@ -441,6 +482,9 @@ mx_status mx_linear(int elem, int layout, int64_t N, int64_t K, const void *w_pa
         g.bias = static_cast<const uint16_t *>(bias);
         g.y = static_cast<uint16_t *>(y);
         g.ldy = ldy;
+        log_dispatch("linear: gemm_w8a8_kernel %s, %d x 256 tiles; M=%lld N=%lld K=%lld",
+                     layout_name(layout), mx::gemm_tile_n(N), (long long)M, (long long)N,
+                     (long long)K);
         return launched(mx::launch_gemm(layout, g, s));
     }
     if (act != ACT_BF16 && w8.ok) {
@@ -462,6 +506,12 @@ mx_status mx_linear(int elem, int layout, int64_t N, int64_t K, const void *w_pa
             g.xc = ac;
             g.ldc = lc;
         }
+        log_dispatch("linear: %s %s, %s activations, %d waves x %d steps x %d tiles; "
+                     "M=%lld N=%lld K=%lld",
+                     mx::gemv_w8_even(N, K, w8) ? (a16 ? "gemv_w8_even_kernel" : "gemv_w8_rm_kernel")
+                                                : "gemv_w8_kernel",
+                     layout_name(layout), a16 ? "T16" : "row-major", w8.nw, w8.spw, w8.g,
+                     (long long)M, (long long)N, (long long)K);
         return launched(mx::launch_gemv_w8(layout, a16, g, w8, s));
     }
     if (a16) return MX_ERR_UNSUPPORTED;             // T16 input with K beyond the GEMV plan
@@ -486,7 +536,12 @@ mx_status mx_linear(int elem, int layout, int64_t N, int64_t K, const void *w_pa
     a.bias = static_cast<const uint16_t *>(bias);
     a.y = static_cast<uint16_t *>(y);
     a.ldy = ldy;
-    return launched(mx::launch_gemv(elem, layout, act, false, a, gemv_shape(Kp / 128, false), s));
+    const mx::GemvShape sh = gemv_shape(Kp / 128, false);
+    log_dispatch("linear: gemv_kernel %s %s, %s activations, %d waves x %d-step chunks x %d "
+                 "tiles; M=%lld N=%lld K=%lld",
+                 elem_name(elem), layout_name(layout), act == ACT_BF16 ? "bf16" : "row-major MXFP8",
+                 sh.nw, sh.chunk, sh.tiles, (long long)M, (long long)N, (long long)K);
+    return launched(mx::launch_gemv(elem, layout, act, false, a, sh, s));
 }
 
 mx_status mx_moe_workspace(int elem, int64_t E, int64_t N, int64_t K, int64_t T, int64_t topk,

@@ -87,6 +87,7 @@ hipError_t launch_moe_combine(int64_t, int64_t, int64_t, const float *, const fl
     return counted();
 }
 hipError_t launch_gemm(int, const GemmArgs &, hipStream_t) { return counted(); }
+int gemm_tile_n(int64_t N) { return N % 224 == 0 && (N / 224) % 8 == 0 ? 224 : 256; }
 hipError_t launch_gemv_w8(int, bool, const GemvW8Args &, const GemvW8Plan &, hipStream_t) {
     return counted();
 }

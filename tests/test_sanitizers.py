@@ -37,8 +37,7 @@ def _env(asan, **extra):
     return env
 
 
-def test_host_code_under_sanitizers(tmp_path):
-    asan = _asan_runtime()
+def _host_lib(tmp_path):
     lib = str(tmp_path / "libmx_host_san.so")
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-D__HIP_PLATFORM_AMD__",
            "-I/opt/rocm/include", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
@@ -49,10 +48,34 @@ def test_host_code_under_sanitizers(tmp_path):
     if r.returncode != 0 and "hip_runtime.h" in r.stderr:
         pytest.skip("HIP headers not found")
     assert r.returncode == 0, r.stderr[-3000:]
+    return lib
+
+
+def test_host_code_under_sanitizers(tmp_path):
+    asan = _asan_runtime()
+    lib = _host_lib(tmp_path)
     r = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "sanitize", "host_checks.py"),
                         lib], capture_output=True, text=True, env=_env(asan), timeout=600)
     assert r.returncode == 0, (r.stdout + r.stderr)[-4000:]
     assert "host checks ok" in r.stdout
+    assert "mx: " not in r.stderr, "dispatch trace printed without MX_LOG"
+
+
+def test_dispatch_trace(tmp_path):
+    """MX_LOG=1: one stderr line per launch decision, naming the kernel and its
+    plan, for every family of the hot path (run on the sanitized host build,
+    whose fake gfx950 device lets every dispatch through to counting stubs)."""
+    asan = _asan_runtime()
+    lib = _host_lib(tmp_path)
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "sanitize", "host_checks.py"),
+                        lib], capture_output=True, text=True, env=_env(asan, MX_LOG="1"),
+                       timeout=600)
+    assert r.returncode == 0, (r.stdout + r.stderr)[-4000:]
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("mx: ")]
+    for kernel in ("gemv_w8_fused_kernel", "gemm_w8a8_kernel", "quant_act_t16_kernel",
+                   "gemv_kernel", "moe_combine_kernel"):
+        assert any(kernel in ln for ln in lines), f"no trace line for {kernel}"
+    assert all("M=" in ln or "T=" in ln for ln in lines)
 
 
 def test_oracle_pins_under_sanitizers(tmp_path):
