@@ -379,18 +379,20 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_even_kernel(GemvW8Args p) {
 // (r, j) is the code of block j of the step, which a lane pair computes; one
 // lane permute brings it to the lane that needs it.
 //
-// Order: the raw activations of all the wavefront's steps first (L2 hits,
-// they arrive long before the weights), then the weight chunks of the first
-// step and the weight codes; each step is quantized just before its MFMAs
-// (its LDS transpose one step earlier), after which the next step's weight
-// chunks are requested.  One step of
-// weight chunks in flight per wavefront (1,792 wavefronts, 7 MB in flight)
-// measured fastest on MI355X: deeper windows, and activations requested with
-// the weights of their step instead of all first, were slower.  Results are
+// Order: the raw activations of the wavefront's first (up to) four steps
+// first (L2 hits, they arrive long before the weights), then the weight
+// chunks of the first step and the weight codes; each step is quantized just
+// before its MFMAs (its LDS transpose one step earlier), after which the
+// activations of the step four ahead and the next step's weight chunks are
+// requested.  One step of weight chunks in flight per wavefront (1,792
+// wavefronts, 7 MB in flight) measured fastest on MI355X: deeper windows,
+// and activations requested with the weights of their own step, were
+// slower.  Results are
 // identical to mx_quant_act_t16 followed by the even-shape kernel: the same
 // bytes, codes and MFMA order.
 template <int LAYOUT, int RULE, int G, int SPW, int NW>
 __global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
+    constexpr int XA = SPW > 4 ? 4 : SPW;              // steps of activations requested first
     constexpr int WIN = 1;                             // steps of weight chunks in flight
     constexpr int XROW = 272;                          // padded LDS row of one token
     __shared__ v4f red[NW][G][64];
@@ -416,11 +418,21 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
         xo[u] = tok < p.M ? (uint32_t)(tok * p.ldx * 2) + 16 * r : kOOB;
     }
     v4u xv[SPW][4];
-#pragma unroll
-    for (int i = 0; i < SPW; ++i)
+    auto xload = [&](int i) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
             xv[i][u] = __builtin_amdgcn_raw_buffer_load_b128(xr, xo[u], (int)(256 * (s0 + i)), 0);
+    };
+    // The first XA steps' activations go out before any weight request;
+    // step i + XA's go out in step i, ahead of that step's weight refill.
+    // Measured on MI355X (M = 16, N = K = 7168, seven steps a wavefront):
+    // all seven up front 11.23 us, four 11.07 us, five 11.17, six 11.14,
+    // three 11.19, two 11.42; M = 1 and 4: 10.26 against 10.68-10.70 us.
+    // Fewer up front lets the first weight requests of all eight
+    // wavefronts out sooner (a CU's address unit takes each wavefront's
+    // activation loads in turn); too few put the later ones in the chain.
+#pragma unroll
+    for (int i = 0; i < XA; ++i) xload(i);
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 2. the first WIN steps of weight chunks ----
@@ -517,6 +529,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
                 (int)cx);
         // the refill goes out right behind this step's MFMAs (left alone,
         // the scheduler sinks it next to its use and exposes its latency)
+        if constexpr (XA < SPW && i + XA < SPW) xload(i + XA);
         if constexpr (i + WIN < SPW) wload(i + WIN);
         if constexpr (i + 1 < SPW) {
 #pragma unroll
