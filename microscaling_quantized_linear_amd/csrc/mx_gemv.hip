@@ -527,6 +527,9 @@ gemv_kernel(GemvArgs p) {
 // Deterministic top-k combine: y[t][n] = sum_k w[t][k] * ys[t*topk + k][n],
 // k ascending, fp32, one bf16 rounding.  A thread owns 4 consecutive outputs
 // (N % 16 == 0) and issues the loads of 8 slots before summing them in order.
+// One-wavefront workgroups spread the launch over as many CUs as it has
+// wavefronts (192 at T = 16, N = 3072; measured on MI355X: MoE block step
+// 46.77 against 46.92 us with 256-thread workgroups).
 __global__ void __launch_bounds__(256) moe_combine_kernel(int64_t T, int64_t topk, int64_t N,
                                                           const float *__restrict__ ys,
                                                           const float *__restrict__ wts,
@@ -607,7 +610,7 @@ hipError_t launch_gemv(int elem, int layout, int act, bool moe, const GemvArgs &
 hipError_t launch_moe_combine(int64_t T, int64_t topk, int64_t N, const float *ys,
                               const float *wts, void *y, hipStream_t st) {
     const int64_t n = T * N / 4;
-    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, T,
+    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, st, T,
                        topk, N, ys, wts, (uint16_t *)y);
     return hipGetLastError();
 }
