@@ -453,33 +453,43 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
     // ---- 3. weight codes: the byte of each step (byte u of a code dword is
     // step 4 q + u), loaded as a byte so no register array is indexed by the
     // wavefront's runtime quad offset ----
-    uint32_t cws[SPW][G];
+    // the code dwords of the quads the wavefront's steps span (byte u of a
+    // dword is step 4 q + u; a quad past the last one reads zeros through
+    // the resource bounds or codes that go unused); each step's byte is
+    // picked by a wavefront-uniform select and shift
+    constexpr int NQ = (SPW + 6) / 4;
+    const uint32_t qa = s0 / 4, a0 = s0 % 4;
+    uint32_t cwd[G][NQ];
     if constexpr (LAYOUT == BLK32) {
         // tiles 2 R and 2 R + 1 share the codes of row group R
         const __amdgpu_buffer_rsrc_t cr = make_rsrc(p.codes, (uint32_t)(p.N / 32) * Q * 16);
 #pragma unroll
-        for (int i = 0; i < SPW; ++i)
+        for (int g = 0; g < G; ++g)
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
+            for (int c = 0; c < NQ; ++c) {
                 if (G % 2 == 0 && g % 2 == 1) {
-                    cws[i][g] = cws[i][g - 1];
+                    cwd[g][c] = cwd[g - 1][c];
                     continue;
                 }
-                const uint32_t s = s0 + i;
-                cws[i][g] = __builtin_amdgcn_raw_buffer_load_b8(
-                    cr, 4 * j, (int)((((t0 + g) / 2) * Q + s / 4) * 16 + s % 4), 0);
+                cwd[g][c] = __builtin_amdgcn_raw_buffer_load_b32(
+                    cr, 4 * j, (int)((((t0 + g) / 2) * Q + qa + c) * 16), 0);
             }
     } else {
         const __amdgpu_buffer_rsrc_t cr = make_rsrc(p.codes, (uint32_t)(p.N / 16) * Q * 256);
 #pragma unroll
-        for (int i = 0; i < SPW; ++i)
+        for (int g = 0; g < G; ++g)
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const uint32_t s = s0 + i;
-                cws[i][g] = __builtin_amdgcn_raw_buffer_load_b8(
-                    cr, 4 * lane, (int)(((t0 + g) * Q + s / 4) * 256 + s % 4), 0);
-            }
+            for (int c = 0; c < NQ; ++c)
+                cwd[g][c] = __builtin_amdgcn_raw_buffer_load_b32(
+                    cr, 4 * lane, (int)(((t0 + g) * Q + qa + c) * 256), 0);
     }
+    auto wcode = [&](int g, int i) -> uint32_t {
+        const uint32_t k = a0 + (uint32_t)i;            // uniform: step s0 + i is quad qa + k / 4
+        uint32_t d = cwd[g][0];
+#pragma unroll
+        for (int c = 1; c < NQ; ++c) d = k >= 4u * c ? cwd[g][c] : d;
+        return (d >> (8 * (k & 3u))) & 0xFFu;
+    };
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 4. per step: transpose, quantize, one scaled MFMA per tile, refill ----
@@ -525,7 +535,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
 #pragma unroll
         for (int g = 0; g < G; ++g)
             acc[g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                cat8(wv[i][g][0], wv[i][g][1]), bq, acc[g], 0, 0, 0, (int)cws[i][g], 0,
+                cat8(wv[i][g][0], wv[i][g][1]), bq, acc[g], 0, 0, 0, (int)wcode(g, i), 0,
                 (int)cx);
         // the refill goes out right behind this step's MFMAs (left alone,
         // the scheduler sinks it next to its use and exposes its latency)
