@@ -629,8 +629,8 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_rm_kernel(GemvW8Args p) {
                 xr, (lds_void_w8 *)(myx + (2 * i + u) * 1024), 16, (int)xo[u],
                 (int)(128 * (s0 + i)), 0, 0);
 
-    // ---- 3. codes: the activation's from the row-major codes, the weights'
-    // one byte per step (byte u of a code dword is step 4 q + u) ----
+    // ---- 3. codes: the activation's from the row-major codes, one byte per
+    // step; the weights' from their dwords (byte u is step 4 q + u) ----
     const __amdgpu_buffer_rsrc_t xcr = make_rsrc(p.xc, (uint32_t)(p.M * p.ldc));
     const int64_t tr = 16 * (int64_t)mb + r;
     const uint32_t cxo = tr < p.M ? (uint32_t)(tr * p.ldc) + (uint32_t)j : kOOB;
@@ -638,32 +638,40 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_rm_kernel(GemvW8Args p) {
 #pragma unroll
     for (int i = 0; i < SPW; ++i)
         cx[i] = __builtin_amdgcn_raw_buffer_load_b8(xcr, cxo, (int)(4 * (s0 + i)), 0);
-    uint32_t cws[SPW][G];
+    // the weights': one dword per quad the wavefront's steps span, each
+    // step's byte picked by a wavefront-uniform select and shift
+    constexpr int NQ = (SPW + 6) / 4;
+    const uint32_t qa = s0 / 4, a0 = s0 % 4;
+    uint32_t cwd[G][NQ];
     if constexpr (LAYOUT == BLK32) {
         const __amdgpu_buffer_rsrc_t cr = make_rsrc(p.codes, (uint32_t)(p.N / 32) * Q * 16);
 #pragma unroll
-        for (int i = 0; i < SPW; ++i)
+        for (int g = 0; g < G; ++g)
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
+            for (int c = 0; c < NQ; ++c) {
                 if (G % 2 == 0 && g % 2 == 1) {
-                    cws[i][g] = cws[i][g - 1];
+                    cwd[g][c] = cwd[g - 1][c];
                     continue;
                 }
-                const uint32_t s = s0 + i;
-                cws[i][g] = __builtin_amdgcn_raw_buffer_load_b8(
-                    cr, 4 * j, (int)((((t0 + g) / 2) * Q + s / 4) * 16 + s % 4), 0);
+                cwd[g][c] = __builtin_amdgcn_raw_buffer_load_b32(
+                    cr, 4 * j, (int)((((t0 + g) / 2) * Q + qa + c) * 16), 0);
             }
     } else {
         const __amdgpu_buffer_rsrc_t cr = make_rsrc(p.codes, (uint32_t)(p.N / 16) * Q * 256);
 #pragma unroll
-        for (int i = 0; i < SPW; ++i)
+        for (int g = 0; g < G; ++g)
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                const uint32_t s = s0 + i;
-                cws[i][g] = __builtin_amdgcn_raw_buffer_load_b8(
-                    cr, 4 * lane, (int)(((t0 + g) * Q + s / 4) * 256 + s % 4), 0);
-            }
+            for (int c = 0; c < NQ; ++c)
+                cwd[g][c] = __builtin_amdgcn_raw_buffer_load_b32(
+                    cr, 4 * lane, (int)(((t0 + g) * Q + qa + c) * 256), 0);
     }
+    auto wcode = [&](int g, int i) -> uint32_t {
+        const uint32_t k = a0 + (uint32_t)i;
+        uint32_t d = cwd[g][0];
+#pragma unroll
+        for (int c = 1; c < NQ; ++c) d = k >= 4u * c ? cwd[g][c] : d;
+        return (d >> (8 * (k & 3u))) & 0xFFu;
+    };
     __builtin_amdgcn_sched_barrier(0);
 
     // ---- 4. the remaining weight chunks ----
@@ -692,7 +700,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_rm_kernel(GemvW8Args p) {
 #pragma unroll
         for (int g = 0; g < G; ++g)
             acc[g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                cat8(wv[i][g][0], wv[i][g][1]), bq, acc[g], 0, 0, 0, (int)cws[i][g], 0,
+                cat8(wv[i][g][0], wv[i][g][1]), bq, acc[g], 0, 0, 0, (int)wcode(g, i), 0,
                 (int)cx[i]);
     });
 
