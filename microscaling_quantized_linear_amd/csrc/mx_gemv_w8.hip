@@ -390,7 +390,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_even_kernel(GemvW8Args p) {
 // slower.  Results are
 // identical to mx_quant_act_t16 followed by the even-shape kernel: the same
 // bytes, codes and MFMA order.
-template <int LAYOUT, int RULE, int G, int SPW, int NW>
+template <int LAYOUT, int RULE, int G, int SPW, int NW, bool FULL>
 __global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
     constexpr int XA = SPW > 4 ? 4 : SPW;              // steps of activations requested first
     constexpr int WIN = 1;                             // steps of weight chunks in flight
@@ -418,10 +418,21 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
         xo[u] = tok < p.M ? (uint32_t)(tok * p.ldx * 2) + 16 * r : kOOB;
     }
     v4u xv[SPW][4];
+    // FULL: every token tile of the call is whole (M % 16 == 0).  Otherwise
+    // a load whose four tokens all lie past M is not issued (a uniform
+    // branch): its registers hold zeros, what the resource bounds would give.
+    // Measured on MI355X: M = 1 9.77 against 10.15 us and M = 4 9.90 against
+    // 10.18 us; the branches cost M = 16 about 0.2 us, hence the two forms.
+    const int64_t mrem = p.M - 16 * (int64_t)mb;       // tokens of this tile
     auto xload = [&](int i) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            xv[i][u] = __builtin_amdgcn_raw_buffer_load_b128(xr, xo[u], (int)(256 * (s0 + i)), 0);
+        for (int u = 0; u < 4; ++u) {
+            if (FULL || 4 * u < mrem)
+                xv[i][u] =
+                    __builtin_amdgcn_raw_buffer_load_b128(xr, xo[u], (int)(256 * (s0 + i)), 0);
+            else
+                xv[i][u] = v4u{0u, 0u, 0u, 0u};
+        }
     };
     // The first XA steps' activations go out before any weight request;
     // step i + XA's go out in step i, ahead of that step's weight refill.
@@ -749,25 +760,32 @@ static hipError_t even_dispatch(const GemvW8Plan &pl, F &&f) {
     }
 }
 
-hipError_t launch_gemv_w8_fused(int layout, int rule, const GemvW8Args &a, const GemvW8Plan &pl,
-                                hipStream_t st) {
-    if (!gemv_w8_even(a.N, a.K, pl) || a.K % 128 != 0) return hipErrorInvalidValue;
+template <bool FULL>
+static hipError_t launch_fused(int layout, int rule, const GemvW8Args &a, const GemvW8Plan &pl,
+                               hipStream_t st) {
     const dim3 grid((unsigned)(a.N / 16 / pl.g), (unsigned)((a.M + 15) / 16)), block(512);
-    const hipError_t e = even_dispatch(pl, [&](auto gc, auto sc) -> hipError_t {
+    return even_dispatch(pl, [&](auto gc, auto sc) -> hipError_t {
         constexpr int G = decltype(gc)::value, SPW = decltype(sc)::value;
         if (layout == ROW32) {
             if (rule == RULE_OCP)
-                hipLaunchKernelGGL((gemv_w8_fused_kernel<ROW32, RULE_OCP, G, SPW, 8>), grid, block, 0, st, a);
+                hipLaunchKernelGGL((gemv_w8_fused_kernel<ROW32, RULE_OCP, G, SPW, 8, FULL>), grid, block, 0, st, a);
             else
-                hipLaunchKernelGGL((gemv_w8_fused_kernel<ROW32, RULE_CEIL448, G, SPW, 8>), grid, block, 0, st, a);
+                hipLaunchKernelGGL((gemv_w8_fused_kernel<ROW32, RULE_CEIL448, G, SPW, 8, FULL>), grid, block, 0, st, a);
         } else {
             if (rule == RULE_OCP)
-                hipLaunchKernelGGL((gemv_w8_fused_kernel<BLK32, RULE_OCP, G, SPW, 8>), grid, block, 0, st, a);
+                hipLaunchKernelGGL((gemv_w8_fused_kernel<BLK32, RULE_OCP, G, SPW, 8, FULL>), grid, block, 0, st, a);
             else
-                hipLaunchKernelGGL((gemv_w8_fused_kernel<BLK32, RULE_CEIL448, G, SPW, 8>), grid, block, 0, st, a);
+                hipLaunchKernelGGL((gemv_w8_fused_kernel<BLK32, RULE_CEIL448, G, SPW, 8, FULL>), grid, block, 0, st, a);
         }
         return hipSuccess;
     });
+}
+
+hipError_t launch_gemv_w8_fused(int layout, int rule, const GemvW8Args &a, const GemvW8Plan &pl,
+                                hipStream_t st) {
+    if (!gemv_w8_even(a.N, a.K, pl) || a.K % 128 != 0) return hipErrorInvalidValue;
+    const hipError_t e = a.M % 16 == 0 ? launch_fused<true>(layout, rule, a, pl, st)
+                                       : launch_fused<false>(layout, rule, a, pl, st);
     if (e != hipSuccess) return e;
     return hipGetLastError();
 }
