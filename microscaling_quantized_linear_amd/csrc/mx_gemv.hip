@@ -219,15 +219,26 @@ gemv_kernel(GemvArgs p) {
         const int64_t npairs = p.rows * p.topk;
         if (wave == 0) {
             int running = 0;
-            for (int64_t base = 0; base < npairs; base += 64) {
-                const int64_t i = base + lane;
-                // unit e == E collects the pairs whose id is out of range
-                const int32_t id = i < npairs ? p.ids[i] : 0;
-                const bool hit = i < npairs && (e < p.E ? id == (int32_t)e : (id < 0 || id >= p.E));
-                const uint64_t mask = __ballot(hit);
-                const int rank = running + __popcll(mask & ((1ull << lane) - 1ull));
-                if (hit) slots[rank] = (uint16_t)i;
-                running += __popcll(mask);
+            // 128 pairs an iteration: both ids loads go out before the first
+            // ballot, so the scan waits for one load round trip, not two
+            for (int64_t base = 0; base < npairs; base += 128) {
+                int32_t id[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int64_t i = base + 64 * h + lane;
+                    id[h] = i < npairs ? p.ids[i] : 0;
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int64_t i = base + 64 * h + lane;
+                    // unit e == E collects the pairs whose id is out of range
+                    const bool hit = i < npairs && (e < p.E ? id[h] == (int32_t)e
+                                                            : (id[h] < 0 || id[h] >= p.E));
+                    const uint64_t mask = __ballot(hit);
+                    const int rank = running + __popcll(mask & ((1ull << lane) - 1ull));
+                    if (hit) slots[rank] = (uint16_t)i;
+                    running += __popcll(mask);
+                }
             }
             if (lane == 0) nslots_sh = running;
         }
