@@ -133,8 +133,10 @@ gemv_kernel(GemvArgs p) {
     // valid prefix of tailb bytes (no padding stored)
     const int64_t TILEB = 16 * (ELEM == E4M3 ? p.K : p.K / 2);
     const uint32_t tailb = (uint32_t)(TILEB - (S - 1) * CHUNK);
-    const __amdgpu_buffer_rsrc_t wr =
-        make_rsrc(p.w + (e * T + t0) * TILEB, (uint32_t)(ntiles * TILEB));
+    // kPre (below): the MoE unit e == E reads no weights, an empty resource
+    constexpr bool kPre = MOE && ELEM == E2M1 && ACT == ACT_BF16 && NW == 2 && P == 2;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(
+        p.w + (e * T + t0) * TILEB, kPre && e >= p.E ? 0u : (uint32_t)(ntiles * TILEB));
     __amdgpu_buffer_rsrc_t cr;
     if (LAYOUT == ROW32)
         cr = make_rsrc(p.codes + (e * T + t0) * Q * 256, (uint32_t)(ntiles * Q * 256));
@@ -213,10 +215,38 @@ gemv_kernel(GemvArgs p) {
         }
         return st;
     };
+    // the E2M1 codes of step s alone (the prefetched chunk's, after the scan)
+    auto loadc_e2m1 = [&](StepA16<G> &st, int64_t s) {
+        const bool in = s < s1;
+#pragma unroll
+        for (int g = 0; g < G; ++g) st.cw[g] = load4(cr, coff(g, s, in, j));
+    };
+
+    // Two-wavefront grouped A16W4 (the short-K down projection): the first
+    // chunk's weight bytes are requested before the routing scan is known
+    // (its codes after it), so the weight stream starts at once.  Wavefront 0 requests them
+    // right behind its first ids loads (loads complete in issue order: the
+    // scan waits for the ids only, not for the weight bytes).
+    static_assert(!kPre || kPairCodes, "the prefetch takes a chunk of two steps");
+    StepA16<G> pre[kPre ? P : 1];
+    auto prefetch = [&]() {
+        pre[0] = loadw(s0, false);
+        pre[1] = loadw(s0 + 1, false);
+    };
 
     int64_t nslots;
     if (MOE) {
         const int64_t npairs = p.rows * p.topk;
+        // the first 128 pairs' ids, then the prefetch: every wavefront issues
+        // both, unconditionally (ids past the pairs read 0 through the
+        // resource bounds), so nothing waits on them before the scan
+        int32_t id0[2] = {0, 0};
+        if constexpr (kPre) {
+            const __amdgpu_buffer_rsrc_t ir = make_rsrc(p.ids, (uint32_t)(npairs * 4));
+#pragma unroll
+            for (int h = 0; h < 2; ++h) id0[h] = (int32_t)load4(ir, (uint32_t)(4 * (64 * h + lane)));
+            prefetch();
+        }
         if (wave == 0) {
             int running = 0;
             // 128 pairs an iteration: both ids loads go out before the first
@@ -226,7 +256,7 @@ gemv_kernel(GemvArgs p) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const int64_t i = base + 64 * h + lane;
-                    id[h] = i < npairs ? p.ids[i] : 0;
+                    id[h] = kPre && base == 0 ? id0[h] : (i < npairs ? p.ids[i] : 0);
                 }
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
@@ -272,7 +302,10 @@ gemv_kernel(GemvArgs p) {
         if (slot < nslots) {
             if (MOE) {
                 const int64_t pair = slots[slot];
-                xrow = p.xslot ? pair : pair / p.topk;    // one activation row per slot, or per token
+                // one activation row per slot, or per token (kPre: 32-bit
+                // division, pair < kMoeMaxPairs, to stay within its registers)
+                xrow = p.xslot ? pair
+                               : (kPre ? (uint32_t)pair / (uint32_t)p.topk : pair / p.topk);
                 yrow = pair;
             } else {
                 xrow = slot;
@@ -394,7 +427,29 @@ gemv_kernel(GemvArgs p) {
                     acc[g] = c;
                 }
             };
-            for (int64_t c = s0; c < s1; c += P) {
+            int64_t c0 = s0;
+            if constexpr (kPre) {
+                // the first batch's first chunk: weights and codes prefetched
+                if (bi == b_first && c0 < s1) {
+                    StepA16<G> st[P];
+                    // the codes of the chunk's quad, then the activations
+                    st[0] = pre[0];
+                    loadc_e2m1(st[0], c0);
+                    loadx(st[0], c0);
+                    st[1] = pre[1];
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        st[1].cw[g] = st[0].cw[g];
+                        st[1].cw2[g] = st[0].cw2[g];
+                    }
+                    loadx(st[1], c0 + 1);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int u = 0; u < P; ++u) compute(st[u], c0 + u);
+                    c0 += P;
+                }
+            }
+            for (int64_t c = c0; c < s1; c += P) {
                 StepA16<G> st[P];
 #pragma unroll
                 for (int u = 0; u < P; ++u) {
