@@ -538,13 +538,16 @@ def test_moe_copies_refuses_padding(g):
     assert ei.value.status == 4                   # MX_ERR_VALUE
 
 
-def test_moe_max_pairs(g):
+@pytest.mark.parametrize("K", [128, 1024])
+def test_moe_max_pairs(g, K):
     """T * topk at the routing scan's maximum (4096 pairs): the ballot walks 64
     rounds, the slot list is full, and the expert everyone routes to gets 16
-    batches of slots; one pair more is refused before any launch."""
+    batches of slots; one pair more is refused before any launch.  K = 128
+    runs the one-wavefront launch; K = 1024 the two-wavefront one, whose
+    first 128 ids and first weight chunk are requested ahead of the scan."""
     import microscaling_quantized_linear_amd as mx
-    E, N, K, T, topk = 16, 32, 128, 512, 8
-    rng = np.random.default_rng(63)
+    E, N, T, topk = 16, 32, 512, 8
+    rng = np.random.default_rng([63, K])
     w = wl.fp4_bytes(rng, (E, N, K // 2))
     codes = wl.codes(rng, (E * N, K // 32), 120, 132)
     x = wl.activations(rng, (T, K))
