@@ -21,8 +21,9 @@
 // The MFMA accumulates in fp32; the single bf16 rounding happens at the store.
 //
 // Grouped MoE: a workgroup first collects the (token, slot) pairs routed to
-// its expert with a wavefront ballot (in pair order) and exits before reading
-// any weight byte if there are none.  Two runtime modes serve the MoE block:
+// its expert with a wavefront ballot (in pair order) and exits if there are
+// none (before reading any weight byte, except for the first chunk the
+// two-wavefront A16W4 form requests ahead of the scan).  Two runtime modes serve the MoE block:
 // `xslot` reads one activation row per slot (the down projection of the
 // hidden rows), `epi` turns interleaved (gate, up) row pairs into
 // silu(gate) * up, one output per pair ([weights942] moe_copies interleaves
@@ -224,9 +225,10 @@ gemv_kernel(GemvArgs p) {
 
     // Two-wavefront grouped A16W4 (the short-K down projection): the first
     // chunk's weight bytes are requested before the routing scan is known
-    // (its codes after it), so the weight stream starts at once.  Wavefront 0 requests them
-    // right behind its first ids loads (loads complete in issue order: the
-    // scan waits for the ids only, not for the weight bytes).
+    // (its codes after it), so the weight stream starts at once.  Every
+    // wavefront requests them right behind the first 128 pairs' ids loads
+    // (loads complete in issue order: wavefront 0's scan waits for the ids
+    // only, not for the weight bytes).
     static_assert(!kPre || kPairCodes, "the prefetch takes a chunk of two steps");
     StepA16<G> pre[kPre ? P : 1];
     auto prefetch = [&]() {
@@ -274,7 +276,9 @@ gemv_kernel(GemvArgs p) {
         }
         __syncthreads();
         nslots = nslots_sh;
-        if (nslots == 0) return;                     // no token: no weight bytes read
+        // no token: no further weight bytes read (the two-wavefront form
+        // has requested its first chunk already)
+        if (nslots == 0) return;
         if (e == p.E) {                              // out-of-range ids: zero rows
             // (with the SiLU epilogue a 16-row tile gives 8 outputs)
             const int64_t per = p.epi ? 8 : 16;
