@@ -548,9 +548,17 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
                 cat8(wv[i][g][0], wv[i][g][1]), bq, acc[g], 0, 0, 0, (int)wcode(g, i), 0,
                 (int)cx);
         // the refill goes out right behind this step's MFMAs (left alone,
-        // the scheduler sinks it next to its use and exposes its latency)
+        // the scheduler sinks it next to its use and exposes its latency).
+        // Partial token tiles issue the weight refill at raised wave
+        // priority, ahead of the other wavefronts' quantization work:
+        // measured on MI355X, M = 4 9.80 against 9.93 us (M = 1 unchanged);
+        // whole tiles keep the default, where it cost M = 16 0.25 us.
         if constexpr (XA < SPW && i + XA < SPW) xload(i + XA);
-        if constexpr (i + WIN < SPW) wload(i + WIN);
+        if constexpr (i + WIN < SPW) {
+            if constexpr (!FULL) __builtin_amdgcn_s_setprio(3);
+            wload(i + WIN);
+            if constexpr (!FULL) __builtin_amdgcn_s_setprio(0);
+        }
         if constexpr (i + 1 < SPW) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) f[c] = fn[c];
