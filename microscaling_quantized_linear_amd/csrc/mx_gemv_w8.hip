@@ -556,8 +556,10 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
         // the scheduler sinks it next to its use and exposes its latency).
         // Partial token tiles issue the weight refill at raised wave
         // priority, ahead of the other wavefronts' quantization work:
-        // measured on MI355X, M = 4 9.80 against 9.93 us (M = 1 unchanged);
-        // whole tiles do not raise it there, where it cost M = 16 0.25 us.
+        // measured on MI355X, M = 4 9.80 against 9.93 us (M = 1 unchanged).
+        // Whole tiles, which raising it cost 0.25 us at M = 16, instead run
+        // at priority 1 and drop to 0 for the activation load (see the
+        // first loads).
         if constexpr (FULL) __builtin_amdgcn_s_setprio(0);
         if constexpr (XA < SPW && i + XA < SPW) xload(i + XA);
         if constexpr (FULL) __builtin_amdgcn_s_setprio(1);
