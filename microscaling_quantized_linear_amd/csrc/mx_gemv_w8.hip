@@ -370,9 +370,18 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_even_kernel(GemvW8Args p) {
 // Loads: per step, four 1 KB loads of 4 tokens x 256 contiguous bytes (lane
 // l reads token 4 u + l / 16, bytes 16 (l % 16) of the step).  Reading 16
 // tokens x 64 bytes per load instead, with the caller's row stride, measured
-// about 4 us slower per launch on MI355X.  A padded 16 x 272-byte LDS tile per
-// wavefront turns the loads into the fragment order (rows 272 bytes apart
-// keep both the writes and the 16-byte reads free of bank conflicts).
+// about 4 us slower per launch on MI355X.  Whole token tiles (M % 16 == 0,
+// four or more steps a wavefront) copy them straight into a ring of four
+// 4 KB LDS slots per wavefront (buffer loads with an LDS destination): each
+// lane fetches the piece whose 16-byte position in its token's 256-byte row
+// is piece ^ token, so the fragment reads are free of bank conflicts, and a
+// wait counted from the fixed issue order (loads complete in issue order)
+// precedes each step's reads.  Measured on MI355X: M = 16 11.05 against
+// 11.08 us (five alternations, every pair lower), with 69 instead of 132
+// VGPRs.  Partial tiles go through registers, skipping the loads of token
+// groups past M, and a padded 16 x 272-byte LDS tile per wavefront turns
+// them into the fragment order (rows 272 bytes apart keep both the writes
+// and the 16-byte reads free of bank conflicts).
 //
 // Quantization: quant_half_block_cvt, the scaled hardware convert, which
 // gives the bytes of mx_quant_act.  The MFMA's activation scale for lane
@@ -396,7 +405,10 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
     constexpr int WIN = 1;                             // steps of weight chunks in flight
     constexpr int XROW = 272;                          // padded LDS row of one token
     __shared__ v4f red[NW][G][64];
-    __shared__ __attribute__((aligned(16))) uint8_t xt[NW][16 * XROW];
+    // whole tiles: activations straight into a ring of four 4 KB LDS slots
+    constexpr bool kXD = FULL && XA == 4;
+    __shared__ __attribute__((aligned(16))) uint8_t xt[kXD ? 1 : NW][16 * XROW];
+    __shared__ __attribute__((aligned(1024))) uint8_t xd[kXD ? NW : 1][kXD ? 4 * 4096 : 16];
 
     const int lane = threadIdx.x % 64;
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
@@ -424,7 +436,22 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
     // Measured on MI355X: M = 1 9.77 against 10.15 us and M = 4 9.90 against
     // 10.18 us; the branches cost M = 16 about 0.2 us, hence the two forms.
     const int64_t mrem = p.M - 16 * (int64_t)mb;       // tokens of this tile
+    uint32_t xod[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t tok = 16 * (int64_t)mb + 4 * u + j;
+        xod[u] = tok < p.M ? (uint32_t)(tok * p.ldx * 2) + 16 * (r ^ (4 * u + j)) : kOOB;
+    }
+    uint8_t *const myd = xd[kXD ? wave : 0];
     auto xload = [&](int i) {
+        if constexpr (kXD) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    xr, (lds_void_w8 *)(myd + (i % 4) * 4096 + u * 1024), 16, (int)xod[u],
+                    (int)(256 * (s0 + i)), 0, 0);
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             if (FULL || 4 * u < mrem)
@@ -534,13 +561,61 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
         d[2] = *reinterpret_cast<const v4u *>(mine + 128);
         d[3] = *reinterpret_cast<const v4u *>(mine + 144);
     };
-    put(0);
-    get(f);
+    // DMA form: step k's fragment straight from its LDS slot (pieces at
+    // position piece ^ token), after a wait that leaves outstanding only the
+    // loads issued after step k's copies
+    constexpr int NCODE = LAYOUT == BLK32 ? (G % 2 == 0 ? G / 2 : G) * NQ : G * NQ;
+    auto nafter = [](int k) constexpr {
+        // loads issued after step k's four copies, up to the read of step k
+        // (issue order: X_0 .. X_{XA-1} (four each), W_0 .. W_{WIN-1},
+        // codes; then step i issues X_{i+XA} and W_{i+WIN} after reading
+        // step i + 1's fragment)
+        int n = 0;
+        bool seen = false;
+        for (int i = 0; i < XA; ++i) {
+            if (seen) n += 4;
+            if (i == k) seen = true;
+        }
+        if (seen) n += WIN * 2 * G + NCODE;
+        if (k == 0) return n;
+        for (int i = 0; i + 1 < k; ++i) {
+            if (i + XA < SPW) {
+                if (seen) n += 4;
+                if (i + XA == k) seen = true;
+            }
+            if (i + WIN < SPW && seen) n += 2 * G;
+        }
+        return n;
+    };
+    auto getd = [&](v4u (&d)[4], auto kconst) {
+        constexpr int k = decltype(kconst)::value;
+        constexpr int n = nafter(k);
+        static_assert(n >= 0 && n < 64, "vmcnt holds 6 bits");
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(vmcnt_only(n));
+        __builtin_amdgcn_sched_barrier(0);
+        const uint8_t *row = myd + (k % 4) * 4096 + r * 256;
+        d[0] = *reinterpret_cast<const v4u *>(row + 16 * ((2 * j) ^ r));
+        d[1] = *reinterpret_cast<const v4u *>(row + 16 * ((2 * j + 1) ^ r));
+        d[2] = *reinterpret_cast<const v4u *>(row + 16 * ((8 + 2 * j) ^ r));
+        d[3] = *reinterpret_cast<const v4u *>(row + 16 * ((9 + 2 * j) ^ r));
+    };
+    if constexpr (kXD) {
+        getd(f, std::integral_constant<int, 0>{});
+    } else {
+        put(0);
+        get(f);
+    }
     static_for<0, SPW>([&](auto iconst) {
         constexpr int i = decltype(iconst)::value;
-        if constexpr (i + 1 < SPW) put(i + 1);
+        if constexpr (!kXD && i + 1 < SPW) put(i + 1);
         const v4u f0 = f[0], f1 = f[1], f2 = f[2], f3 = f[3];
-        if constexpr (i + 1 < SPW) get(fn);
+        if constexpr (i + 1 < SPW) {
+            if constexpr (kXD)
+                getd(fn, std::integral_constant<int, i + 1>{});
+            else
+                get(fn);
+        }
         uint32_t c0, c1;
         const v4u q0 = quant_half_block_cvt<RULE>(f0, f1, c0);
         const v4u q1 = quant_half_block_cvt<RULE>(f2, f3, c1);
@@ -562,6 +637,7 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
         // first loads).
         if constexpr (FULL) __builtin_amdgcn_s_setprio(0);
         if constexpr (XA < SPW && i + XA < SPW) xload(i + XA);
+        if constexpr (kXD) __builtin_amdgcn_sched_barrier(0);
         if constexpr (FULL) __builtin_amdgcn_s_setprio(1);
         if constexpr (i + WIN < SPW) {
             if constexpr (!FULL) __builtin_amdgcn_s_setprio(3);

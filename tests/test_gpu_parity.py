@@ -373,7 +373,10 @@ def test_linear_t16_equals_in_call(g, layout, M, N, K):
 # ------------------------------------------------------------------ fused quantization
 
 FUSED_SHAPES = [(1, 64, 1024), (2, 96, 2048), (15, 256, 4096), (16, 1792, 7168), (17, 64, 8192),
-                (33, 32, 1024), (64, 128, 2048), (4, 7168, 7168)]
+                (33, 32, 1024), (64, 128, 2048), (4, 7168, 7168),
+                # whole token tiles at four and eight steps a wavefront (the
+                # activation copies go into a ring of LDS slots)
+                (16, 256, 4096), (32, 64, 8192)]
 
 
 @pytest.mark.parametrize("layout", [ROW32, BLK32])
