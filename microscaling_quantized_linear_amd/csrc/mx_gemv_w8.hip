@@ -436,6 +436,9 @@ __global__ void __launch_bounds__(NW * 64) gemv_w8_fused_kernel(GemvW8Args p) {
     // Measured on MI355X: M = 1 9.77 against 10.15 us and M = 4 9.90 against
     // 10.18 us; the branches cost M = 16 about 0.2 us, hence the two forms.
     const int64_t mrem = p.M - 16 * (int64_t)mb;       // tokens of this tile
+    // LDS-destination form: copy u lands lane (r, j)'s 16 bytes at position
+    // r of token 4 u + j's 256-byte row in the slot, so the lane fetches the
+    // piece r ^ (4 u + j): piece p of token n sits at position p ^ n
     uint32_t xod[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
